@@ -1,0 +1,163 @@
+/*
+ * kdkl.h - C ABI of the fused, chunked top-K KL distillation loss over an LM head,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages about arXiv 2608.03796, "Efficient Knowledge Distillation for
+ * LLMs: Offline Top-K Logits and a Fused Chunked KL Loss"):
+ *   [abs]  the paper's abstract (chatpaper.ai page / Hugging Face papers mirror):
+ *          offline KD caches the teacher's top-K logits once; the fused chunked KL
+ *          loss never materialises the full vocabulary-sized logit tensor, so peak
+ *          memory grows linearly with sequence length.
+ *   [mv]   mind-verse.de, "Optimierung der Wissensdestillation ...", section
+ *          "2. Ein zusammengeführter, chunked KL-Verlust", bullet "Fused chunked KL":
+ *          the output projection is folded into the loss, one chunk at a time is
+ *          projected, folded into the running loss and discarded; the backward pass
+ *          recomputes each chunk, so the projection runs twice.
+ *   [wiki] llm-wiki study note "LLM 지식 증류 효율화 ...", sections "표준 KD의 손실 함수"
+ *          (KL(P_T || P_S) over the vocabulary), "핵심 아이디어 1: Offline Top-K Logits"
+ *          (K (vocab index, logit) pairs per position), "기존 라이브러리 통합" (the
+ *          teacher precompute and the fused loss are independent, drop-in pieces).
+ *
+ * Notation: N tokens, d hidden size, V vocabulary, K cached entries per token.
+ *   H [N, d]   student final hidden states            (row-major)
+ *   W [V, d]   student LM head, out x in (no bias)     (row-major)
+ *   H_T, W_T   teacher hidden states / teacher head    (same layouts)
+ *   idx [N, K] int32 cached vocabulary indices        (row-major)
+ *   val [N, K] cached teacher logits                   (row-major)
+ *
+ * What is computed (all rows count; mean over N):
+ *   z[i,v]  = H[i,:] . W[v,:]                 student logits (never stored)
+ *   lse[i]  = log sum_v exp(z[i,v])           over the whole vocabulary
+ *   p[i,k]  = softmax_k(val[i,k] / tau)       teacher renormalised over its K entries
+ *   KL[i]   = sum_k p[i,k] (log p[i,k] - z[i,idx[i,k]] + lse[i])   (p log p = 0 at p = 0)
+ *   loss    = (1/N) sum_i KL[i]
+ *   dZ[i,v] = (g/N) (exp(z[i,v] - lse[i]) - sum_{k: idx[i,k]=v} p[i,k])
+ *   dH = dZ W,  dW = dZ^T H
+ * tau applies to the teacher only (no tau^2 factor). Repeated indices in a row are
+ * separate entries (the gradient scatter-adds them).
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers into contiguous row-major buffers,
+ *     16-byte aligned. The caller owns every buffer; the library allocates no
+ *     device memory and keeps no state besides a per-device architecture check.
+ *   - Scratch memory is the caller's workspace `ws` of at least
+ *     kd_workspace_size() bytes (16-byte aligned); its contents on entry do not
+ *     matter and are clobbered.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *     the call returns without waiting. Two calls that share a workspace must be
+ *     ordered on one stream.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Errors: every argument error returns a non-zero kd_status BEFORE anything is
+ *     enqueued or any HIP call is made; KD_ERR_NO_DEVICE / KD_ERR_UNSUPPORTED_ARCH
+ *     come from the device check that follows validation; KD_ERR_LAUNCH reports a
+ *     failed kernel launch. Asynchronous device faults surface at the caller's next
+ *     synchronisation. The library never aborts, prints or throws.
+ *   - Shape domain: N >= 0, d >= 8 with d % 8 == 0, 1 <= V <= 4194304,
+ *     1 <= K <= min(V, 65535) (the cache build: K <= 4096), tau finite and > 0.
+ *   - Cached indices must lie in [0, V). An out-of-range index is skipped by the
+ *     kernels (no out-of-bounds access); it makes that row's KL NaN, and when the
+ *     environment variable KD_CHECK=1 is set the forward call synchronises the
+ *     stream and returns KD_ERR_IDX_OUT_OF_RANGE.
+ *   - Results are bitwise reproducible for a given shape, chunk size and device
+ *     (no floating-point atomics), except the gradient of a row whose cached
+ *     indices repeat.
+ */
+#ifndef KDKL_H
+#define KDKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
+
+typedef enum {
+  KD_OK = 0,
+  KD_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+  KD_ERR_BAD_SHAPE = 2,          /* a size is outside the domain above, or overflows */
+  KD_ERR_BAD_DTYPE = 3,          /* unknown dtype, or an unsupported combination */
+  KD_ERR_BAD_TAU = 4,            /* tau not finite or <= 0 */
+  KD_ERR_MISALIGNED = 5,         /* a pointer is not 16-byte aligned */
+  KD_ERR_WORKSPACE_TOO_SMALL = 6,/* ws_bytes < kd_workspace_size() */
+  KD_ERR_NO_DEVICE = 7,          /* no HIP device is current */
+  KD_ERR_UNSUPPORTED_ARCH = 8,   /* the current device is not gfx950 */
+  KD_ERR_LAUNCH = 9,             /* a kernel launch failed */
+  KD_ERR_IDX_OUT_OF_RANGE = 10,  /* only with KD_CHECK=1: a cached index is outside [0, V) */
+  KD_ERR_TOPK_OVERFLOW = 11      /* only with KD_CHECK=1: too many near-ties at the K-th value */
+} kd_status;
+
+typedef enum { KD_OP_TOPK_BUILD = 0, KD_OP_KL_FWD = 1, KD_OP_KL_BWD = 2 } kd_op;
+
+/* Problem description shared by all calls. */
+typedef struct {
+  int64_t n_tokens;     /* N */
+  int64_t d_model;      /* d */
+  int64_t vocab;        /* V */
+  int32_t k;            /* K */
+  float tau;            /* teacher temperature (KL calls; ignored by the cache build) */
+  int32_t x_dtype;      /* kd_dtype of H, W, H_T, W_T: KD_BF16, or KD_F32 */
+  int32_t val_dtype;    /* kd_dtype of val: KD_BF16 (with bf16 x) or KD_F32 (with f32 x) */
+  int32_t dh_dtype;     /* kd_dtype of dH: KD_F32 or KD_BF16 (dW is always float32) */
+  int32_t chunk_tokens; /* tokens per chunk; 0 = library default. Rounded up to 256. */
+} kd_problem;
+
+/* Workspace bytes that `op` needs for problem `p` (independent of the data).
+ * The workspace grows with the chunk size, not with N, except for O(N) terms
+ * of a few bytes per token. Returns KD_OK and writes *bytes, or an argument error. */
+kd_status kd_workspace_size(kd_op op, const kd_problem* p, size_t* bytes);
+
+/* Offline teacher cache ([abs]; [wiki] "핵심 아이디어 1", "사전 계산 파이프라인"):
+ * S = H_T W_T^T evaluated tile by tile with bf16 (or f32) MFMA, then an exact
+ * per-row top-K. Candidates within a rigorous float32 error bound of the K-th
+ * value are re-scored in float64, so the chosen set and order equal those of the
+ * exact logits. Output rows are sorted by exact logit, descending; equal logits
+ * put the smaller index first.
+ *   h_t   [N, d] x_dtype          w_t [V, d] x_dtype
+ *   idx_out [N, K] int32          val_out [N, K] val_dtype: the exact logit rounded
+ *                                 once (nearest, ties to even) to bf16 / f32.
+ * tau and dh_dtype are ignored. */
+kd_status kd_topk_cache_build(const kd_problem* p, const void* h_t, const void* w_t,
+                              int32_t* idx_out, void* val_out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Forward of the fused chunked KL ([mv] "Fused chunked KL"; [wiki] "표준 KD의 손실 함수").
+ * Student logits are computed tile by tile (tokens x vocabulary) with MFMA; each
+ * tile is folded into a per-row online log-sum-exp and the cached entries are
+ * gathered from it; nothing of size N x V is stored.
+ *   h [N, d], w [V, d] x_dtype;  idx [N, K] int32;  val [N, K] val_dtype
+ *   loss_out   device float scalar: the mean KL over the N rows (0 when N = 0)
+ *   lse_out    [N] float: per-row log-sum-exp (the input of the backward call)
+ *   kl_rows_out[N] float per-row KL, or NULL. */
+kd_status kd_chunked_kl_fwd(const kd_problem* p, const void* h, const void* w,
+                            const int32_t* idx, const void* val,
+                            float* loss_out, float* lse_out, float* kl_rows_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the fused chunked KL ([mv] "Fused chunked KL": the backward pass
+ * recomputes every chunk's logits). For each token chunk: recompute the logit
+ * tiles, form dZ in bf16 (f32 for f32 inputs) in a chunk-sized buffer, then
+ * dH = dZ W and dW += dZ^T H with MFMA; dW is accumulated in float32 in tiles
+ * that each workgroup owns (no atomics).
+ *   lse        [N] float from kd_chunked_kl_fwd on the same inputs
+ *   grad_loss  device float scalar g (d loss_total / d loss), or NULL for g = 1
+ *   dh_out     [N, d] dh_dtype (overwritten)
+ *   dw_out     [V, d] float32  (overwritten; zero when N = 0) */
+kd_status kd_chunked_kl_bwd(const kd_problem* p, const void* h, const void* w,
+                            const int32_t* idx, const void* val,
+                            const float* lse, const float* grad_loss,
+                            void* dh_out, float* dw_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* kd_status_string(kd_status s);
+
+/* Library ABI version (major * 100 + minor). */
+int kd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDKL_H */

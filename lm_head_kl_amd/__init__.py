@@ -1,0 +1,239 @@
+"""Python binding of the kdkl HIP library (fused, chunked top-K KL distillation loss).
+
+Argument marshalling only: every step of the loss runs in the library's HIP
+kernels (``lm_head_kl_amd/csrc``, C ABI in ``include/kdkl.h``).  PyTorch provides
+device memory (through its caching allocator, so peak-memory statistics include
+the workspace) and the current HIP stream.  There is no CPU fallback: if the
+library is missing or a tensor is not on a GPU, the call raises.
+
+Entry points (same names as the C ABI):
+
+* :func:`kd_topk_cache_build` -- offline teacher cache: exact top-K (index,
+  logit) pairs of ``H_T @ W_T^T`` per token.
+* :func:`kd_chunked_kl_fwd` -- loss, per-row log-sum-exp (and per-row KL).
+* :func:`kd_chunked_kl_bwd` -- ``dH`` and ``dW``.
+* :class:`KDChunkedKL` / :func:`chunked_kl_loss` -- autograd wrapper (forward
+  saves ``lse``; backward calls :func:`kd_chunked_kl_bwd`).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkdkl.so")
+
+KD_F32, KD_BF16 = 0, 1
+KD_OP_TOPK_BUILD, KD_OP_KL_FWD, KD_OP_KL_BWD = 0, 1, 2
+
+STATUS_NAMES = {
+    0: "KD_OK", 1: "KD_ERR_NULL_POINTER", 2: "KD_ERR_BAD_SHAPE", 3: "KD_ERR_BAD_DTYPE", 4: "KD_ERR_BAD_TAU",
+    5: "KD_ERR_MISALIGNED", 6: "KD_ERR_WORKSPACE_TOO_SMALL", 7: "KD_ERR_NO_DEVICE", 8: "KD_ERR_UNSUPPORTED_ARCH",
+    9: "KD_ERR_LAUNCH", 10: "KD_ERR_IDX_OUT_OF_RANGE", 11: "KD_ERR_TOPK_OVERFLOW",
+}
+
+# Every symbol the header declares (checked by the CPU test suite).
+EXPORTED = ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd",
+            "kd_status_string", "kd_version")
+
+
+class KDProblem(ctypes.Structure):
+    """Mirror of ``kd_problem`` in include/kdkl.h."""
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("d_model", ctypes.c_int64),
+        ("vocab", ctypes.c_int64),
+        ("k", ctypes.c_int32),
+        ("tau", ctypes.c_float),
+        ("x_dtype", ctypes.c_int32),
+        ("val_dtype", ctypes.c_int32),
+        ("dh_dtype", ctypes.c_int32),
+        ("chunk_tokens", ctypes.c_int32),
+    ]
+
+
+class KDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) the built shared library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"kdkl HIP library not built: {path} is missing "
+                           f"(run `python -m lm_head_kl_amd.build`)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(KDProblem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.kd_workspace_size.argtypes = [ctypes.c_int, P, ctypes.POINTER(sz)]
+    lib.kd_topk_cache_build.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_chunked_kl_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_chunked_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.kd_status_string.argtypes = [ctypes.c_int]
+    lib.kd_status_string.restype = ctypes.c_char_p
+    lib.kd_version.argtypes = []
+    lib.kd_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().kd_status_string(int(status)).decode()
+    except RuntimeError:
+        return STATUS_NAMES.get(status, "unknown")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise KDError(status, where)
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KD_BF16
+    if t == torch.float32:
+        return KD_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def make_problem(n: int, d: int, v: int, k: int, tau: float = 1.0, x_dtype: int = KD_BF16,
+                 val_dtype: Optional[int] = None, dh_dtype: int = KD_F32, chunk_tokens: int = 0) -> KDProblem:
+    return KDProblem(int(n), int(d), int(v), int(k), float(tau), int(x_dtype),
+                     int(x_dtype if val_dtype is None else val_dtype), int(dh_dtype), int(chunk_tokens))
+
+
+def workspace_size(op: int, prob: KDProblem) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().kd_workspace_size(int(op), ctypes.byref(prob), ctypes.byref(out)), "kd_workspace_size")
+    return int(out.value)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_gpu(*ts: torch.Tensor) -> torch.device:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("kdkl works on GPU tensors only (no CPU fallback)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous row-major")
+        dev = t.device if dev is None else dev
+        if t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _workspace(op: int, prob: KDProblem, device: torch.device) -> torch.Tensor:
+    return torch.empty(max(256, workspace_size(op, prob)), dtype=torch.uint8, device=device)
+
+
+def kd_topk_cache_build(h_t: torch.Tensor, w_t: torch.Tensor, k: int, chunk_tokens: int = 0
+                        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact top-K teacher cache.  Returns ``(idx int32 [N,K], val [N,K])``; ``val``
+    has the inputs' dtype (bf16 for bf16 heads, float32 for float32 heads)."""
+    dev = _need_gpu(h_t, w_t)
+    n, d = h_t.shape
+    v = w_t.shape[0]
+    xdt = _dt(h_t.dtype)
+    if _dt(w_t.dtype) != xdt or w_t.shape[1] != d:
+        raise ValueError("h_t / w_t dtype or shape mismatch")
+    prob = make_problem(n, d, v, k, 1.0, xdt, xdt, KD_F32, chunk_tokens)
+    idx = torch.empty((n, k), dtype=torch.int32, device=dev)
+    val = torch.empty((n, k), dtype=h_t.dtype, device=dev)
+    ws = _workspace(KD_OP_TOPK_BUILD, prob, dev)
+    with torch.cuda.device(dev):
+        st = _stream(dev)
+        _check(load_library().kd_topk_cache_build(ctypes.byref(prob), _ptr(h_t), _ptr(w_t), _ptr(idx), _ptr(val),
+                                                  _ptr(ws), ws.numel(), st), "kd_topk_cache_build")
+    return idx, val
+
+
+def kd_chunked_kl_fwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, tau: float,
+                      with_rows: bool = False, chunk_tokens: int = 0
+                      ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """Returns ``(loss [] float32, lse [N] float32, kl_rows [N] float32 or None)``."""
+    dev = _need_gpu(h, w, idx, val)
+    n, d = h.shape
+    v = w.shape[0]
+    k = idx.shape[1]
+    xdt = _dt(h.dtype)
+    if idx.dtype != torch.int32 or val.shape != idx.shape or idx.shape[0] != n:
+        raise ValueError("idx must be int32 [N, K] and val [N, K]")
+    prob = make_problem(n, d, v, k, tau, xdt, _dt(val.dtype), KD_F32, chunk_tokens)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty((n,), dtype=torch.float32, device=dev)
+    rows = torch.empty((n,), dtype=torch.float32, device=dev) if with_rows else None
+    ws = _workspace(KD_OP_KL_FWD, prob, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().kd_chunked_kl_fwd(ctypes.byref(prob), _ptr(h), _ptr(w), _ptr(idx), _ptr(val),
+                                                _ptr(loss), _ptr(lse), _ptr(rows), _ptr(ws), ws.numel(),
+                                                _stream(dev)), "kd_chunked_kl_fwd")
+    return loss, lse, rows
+
+
+def kd_chunked_kl_bwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, tau: float,
+                      lse: torch.Tensor, grad: Optional[torch.Tensor] = None, dh_dtype: torch.dtype = torch.float32,
+                      chunk_tokens: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Returns ``(dH [N,d] dh_dtype, dW [V,d] float32)`` for upstream gradient
+    ``grad`` (a device scalar; None means 1)."""
+    dev = _need_gpu(h, w, idx, val, lse, grad)
+    n, d = h.shape
+    v = w.shape[0]
+    k = idx.shape[1]
+    if grad is not None and (grad.dtype != torch.float32 or grad.numel() != 1):
+        raise ValueError("grad must be a float32 scalar tensor")
+    prob = make_problem(n, d, v, k, tau, _dt(h.dtype), _dt(val.dtype), _dt(dh_dtype), chunk_tokens)
+    dh = torch.empty((n, d), dtype=dh_dtype, device=dev)
+    dw = torch.empty((v, d), dtype=torch.float32, device=dev)
+    ws = _workspace(KD_OP_KL_BWD, prob, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().kd_chunked_kl_bwd(ctypes.byref(prob), _ptr(h), _ptr(w), _ptr(idx), _ptr(val),
+                                                _ptr(lse), _ptr(grad), _ptr(dh), _ptr(dw), _ptr(ws), ws.numel(),
+                                                _stream(dev)), "kd_chunked_kl_bwd")
+    return dh, dw
+
+
+class KDChunkedKL(torch.autograd.Function):
+    """``loss = KDChunkedKL.apply(H, W, idx, val, tau)``; gradients flow to H and W."""
+
+    @staticmethod
+    def forward(ctx, h, w, idx, val, tau, chunk_tokens=0):
+        loss, lse, _ = kd_chunked_kl_fwd(h, w, idx, val, tau, chunk_tokens=chunk_tokens)
+        ctx.save_for_backward(h, w, idx, val, lse)
+        ctx.tau = tau
+        ctx.chunk_tokens = chunk_tokens
+        return loss
+
+    @staticmethod
+    def backward(ctx, g):
+        h, w, idx, val, lse = ctx.saved_tensors
+        g = g.detach().to(torch.float32).reshape(()).contiguous()
+        dh, dw = kd_chunked_kl_bwd(h, w, idx, val, ctx.tau, lse, g,
+                                   dh_dtype=torch.float32 if h.dtype == torch.float32 else torch.bfloat16,
+                                   chunk_tokens=ctx.chunk_tokens)
+        return dh.to(h.dtype), dw.to(w.dtype), None, None, None, None
+
+
+def chunked_kl_loss(h, w, idx, val, tau: float = 1.0, chunk_tokens: int = 0) -> torch.Tensor:
+    return KDChunkedKL.apply(h, w, idx, val, float(tau), int(chunk_tokens))

@@ -1,0 +1,385 @@
+// Non-GEMM kernels of the chunked top-K KL loss and of the teacher-cache build.
+#pragma once
+
+#include "kd_common.hpp"
+#include "kd_gemm.hpp"
+
+namespace kd {
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive prefix sum of one int per thread (blockDim.x <= 1024).
+__device__ __forceinline__ int block_excl_scan(int v, int* sh /* >= 32 ints */, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) { const int t = sh[w]; sh[w] = run; run += t; }
+    sh[31] = run;
+  }
+  __syncthreads();
+  const int r = sh[wave] + x - v;
+  total = sh[31];
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Bucket the cache entries of one 256-token tile by 256-wide vocabulary tile, so
+// the forward GEMM epilogue of tile (tx, ty) reads exactly the entries that fall
+// inside it.  Entry = token (8 bits) | vocab within tile (8 bits) | k (16 bits).
+// Out-of-range indices are skipped and flagged.
+__global__ void __launch_bounds__(1024) bucket_kernel(const int32_t* __restrict__ idx, int nr, int kc, int vocab,
+                                                      int n_ty, uint32_t* __restrict__ entries,
+                                                      int* __restrict__ offsets, int* __restrict__ bad) {
+  extern __shared__ int hist[];   // n_ty + 64 ints
+  int* sh = hist + n_ty + 1;
+  const int tx = blockIdx.x;
+  const int r0 = tx * BX;
+  const int rows = min(BX, nr - r0);
+  const int total = rows * kc;
+  const int32_t* src = idx + (int64_t)r0 * kc;
+  for (int b = threadIdx.x; b <= n_ty; b += blockDim.x) hist[b] = 0;
+  __syncthreads();
+  int nbad = 0;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int v = src[e];
+    if ((unsigned)v < (unsigned)vocab) atomicAdd(&hist[v >> 8], 1);
+    else ++nbad;
+  }
+  if (nbad) atomicAdd(bad, nbad);
+  __syncthreads();
+  // exclusive scan of hist[0..n_ty) in contiguous per-thread segments
+  const int seg = (n_ty + blockDim.x - 1) / blockDim.x;
+  const int b0 = min(n_ty, (int)threadIdx.x * seg), b1 = min(n_ty, b0 + seg);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += hist[b];
+  int tot;
+  int run = block_excl_scan(local, sh, tot);
+  int* out = offsets + (int64_t)tx * (n_ty + 1);
+  for (int b = b0; b < b1; ++b) {
+    const int c = hist[b];
+    hist[b] = run;
+    out[b] = run;
+    run += c;
+  }
+  if (threadIdx.x == 0) out[n_ty] = tot;
+  __syncthreads();
+  uint32_t* dst = entries + (int64_t)tx * BX * kc;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int v = src[e];
+    if ((unsigned)v < (unsigned)vocab) {
+      const int pos = atomicAdd(&hist[v >> 8], 1);
+      const int t = e / kc, k = e - t * kc;
+      dst[pos] = uint32_t(t) | (uint32_t(v & 255) << 8) | (uint32_t(k) << 16);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block sum of one double per thread (256 threads), fixed order.
+__device__ __forceinline__ double block_sum_256(double v, double* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
+    __syncthreads();
+  }
+  return sh[0];
+}
+
+// Merge the per-tile (max, sum exp) partials of each row into lse, form the
+// teacher softmax over the K cached logits and the row's KL, and sum the block's
+// KL values (float64) for the deterministic loss reduction.
+template <typename VT>
+__global__ void __launch_bounds__(256) merge_kernel(const float2* __restrict__ partials, int64_t ld_part, int n_ty,
+                                                    const int32_t* __restrict__ idx, const VT* __restrict__ val,
+                                                    const float* __restrict__ zg, int nr, int kc, int vocab,
+                                                    float inv_tau, float* __restrict__ lse_out,
+                                                    float* __restrict__ kl_out, double* __restrict__ block_sums) {
+  __shared__ double sh[256];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  double kl_d = 0.0;
+  if (t < nr) {
+    float M = -INFINITY, S = 0.f;
+    for (int y = 0; y < n_ty; ++y) {
+      const float2 p = partials[(int64_t)y * ld_part + t];
+      if (p.x > M) {
+        S = S * exp2f((M - p.x) * kLog2e) + p.y;
+        M = p.x;
+      } else if (p.x != -INFINITY) {
+        S += p.y * exp2f((p.x - M) * kLog2e);
+      }
+    }
+    const float lse = M + logf(S);
+    const VT* vr = val + (int64_t)t * kc;
+    const int32_t* ir = idx + (int64_t)t * kc;
+    const float* zr = zg + (int64_t)t * kc;
+    float vmax = -INFINITY;
+    for (int k = 0; k < kc; ++k) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
+    float Z = 0.f;
+    for (int k = 0; k < kc; ++k) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
+    const float logZ = logf(Z);
+    float kl = 0.f;
+    for (int k = 0; k < kc; ++k) {
+      const float lp = to_f32<VT>(vr[k]) * inv_tau - vmax - logZ;
+      const float p = expf(lp);
+      if ((unsigned)ir[k] >= (unsigned)vocab) kl = NAN;
+      else kl += (p > 0.f ? p * lp : 0.f) - p * (zr[k] - lse);
+    }
+    lse_out[t] = lse;
+    if (kl_out) kl_out[t] = kl;
+    kl_d = (double)kl;
+  }
+  const double s = block_sum_256(kl_d, sh);
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = s;
+}
+
+// loss = (sum of block sums) / N, summed in a fixed order.
+__global__ void __launch_bounds__(256) loss_kernel(const double* __restrict__ block_sums, int nb, double inv_n,
+                                                   float* __restrict__ loss) {
+  __shared__ double sh[256];
+  double a = 0.0;
+  for (int b = threadIdx.x; b < nb; b += 256) a += block_sums[b];
+  const double s = block_sum_256(a, sh);
+  if (threadIdx.x == 0) *loss = (float)(s * inv_n);
+}
+
+// ---------------------------------------------------------------------------
+// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rows_pad; c < cols.
+template <typename T>
+__global__ void __launch_bounds__(256) transpose_pad_kernel(const T* __restrict__ src, int64_t ld_src, int rows,
+                                                            int cols, T* __restrict__ dst, int64_t ld_dst,
+                                                            int rows_pad) {
+  __shared__ T tile[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < rows && c < cols) ? src[(int64_t)r * ld_src + c] : T(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows_pad) dst[(int64_t)c * ld_dst + r] = tile[tx][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Subtract the scaled teacher probabilities at the cached entries of each row
+// from dZ and dZ^T.  One thread owns one row, so repeated indices within a row
+// are applied in k order with no race.
+template <typename T, typename VT>
+__global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ idx, const VT* __restrict__ val,
+                                                      int nr, int kc, int vocab, float inv_tau,
+                                                      const float* __restrict__ grad, float inv_n,
+                                                      T* __restrict__ dz, int64_t ldz, T* __restrict__ dzt,
+                                                      int64_t ldzt) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= nr) return;
+  const float scale = (grad ? *grad : 1.0f) * inv_n;
+  const VT* vr = val + (int64_t)t * kc;
+  const int32_t* ir = idx + (int64_t)t * kc;
+  float vmax = -INFINITY;
+  for (int k = 0; k < kc; ++k) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
+  float Z = 0.f;
+  for (int k = 0; k < kc; ++k) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
+  const float logZ = logf(Z);
+  for (int k = 0; k < kc; ++k) {
+    const int v = ir[k];
+    if ((unsigned)v >= (unsigned)vocab) continue;
+    const float pe = scale * expf(to_f32<VT>(vr[k]) * inv_tau - vmax - logZ);
+    T* a = dz + (int64_t)t * ldz + v;
+    *a = from_f32<T>(to_f32<T>(*a) - pe);
+    T* b = dzt + (int64_t)v * ldzt + t;
+    *b = from_f32<T>(to_f32<T>(*b) - pe);
+  }
+}
+
+// Fill a float buffer (used for dW when there are no tokens).
+__global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Teacher cache build.
+// max over rows of the Euclidean norm of W_T (float64), per block then global.
+template <typename T>
+__global__ void __launch_bounds__(256) rownorm_max_kernel(const T* __restrict__ w, int rows, int d,
+                                                          double* __restrict__ block_max) {
+  __shared__ double sh[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double best = 0.0;
+  for (int r = blockIdx.x * 4 + wave; r < rows; r += gridDim.x * 4) {
+    const T* p = w + (int64_t)r * d;
+    double s = 0.0;
+    for (int j = lane; j < d; j += 64) {
+      const double x = (double)to_f32<T>(p[j]);
+      s += x * x;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    best = fmax(best, s);
+  }
+  if (lane == 0) sh[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) block_max[blockIdx.x] = sqrt(fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3])));
+}
+
+__global__ void __launch_bounds__(256) max_reduce_kernel(const double* __restrict__ in, int n,
+                                                         double* __restrict__ out) {
+  __shared__ double sh[256];
+  double m = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmax(m, in[i]);
+  sh[threadIdx.x] = m;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) sh[threadIdx.x] = fmax(sh[threadIdx.x], sh[threadIdx.x + s]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = sh[0];
+}
+
+constexpr int SEL_CAP = 6144;    // candidate capacity per row (K <= 4096)
+constexpr int SEL_THREADS = 256;
+
+// Finds the largest bin B of hist[4096] with count(bins >= B) >= need; writes B and
+// count(bins > B) to res[0], res[1].  256 threads, 16 bins each.
+__device__ __forceinline__ void select_bin(const uint32_t* hist, int need, int* sh, int* res) {
+  const int t = threadIdx.x;
+  int local = 0;
+#pragma unroll
+  for (int b = 0; b < 16; ++b) local += (int)hist[t * 16 + b];
+  // count above this thread's bins = total - inclusive prefix
+  int total;
+  const int excl = block_excl_scan(local, sh, total);
+  const int above = total - excl - local;
+  if (above < need && above + local >= need) {
+    int run = above;
+    for (int b = 15; b >= 0; --b) {
+      const int c = (int)hist[t * 16 + b];
+      if (run + c >= need) {
+        res[0] = t * 16 + b;
+        res[1] = run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+}
+
+// Exact top-K of one teacher row.  s[V] holds the float32 MFMA logits.
+//  1. Two 12-bit radix histograms of the order-preserving key locate a
+//     sub-bin [lo, ...) that contains the K-th largest float32 value T_K.
+//  2. Every value >= lo - 2*eps is a candidate, where eps bounds |fp32 - exact|
+//     for any logit of the row (Higham's summation bound with Cauchy-Schwarz:
+//     eps = 2 d 2^-23 ||h|| max_v ||w_v||).  Every exact top-K member is in the set.
+//  3. Candidates are re-scored exactly-rounded in float64, ranked by (score desc,
+//     index asc), and the first K are written.
+template <typename T, typename VT>
+__global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
+    const float* __restrict__ S, int64_t ld_s, int V, int K, const T* __restrict__ ht, int d,
+    const T* __restrict__ wt, const double* __restrict__ wmax, int32_t* __restrict__ idx_out,
+    VT* __restrict__ val_out, int* __restrict__ overflow) {
+  __shared__ uint32_t hist[4096];
+  __shared__ int cidx[SEL_CAP];
+  __shared__ double cscore[SEL_CAP];
+  __shared__ int sh[40];
+  __shared__ double shd[SEL_THREADS];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* s = S + (int64_t)row * ld_s;
+  const T* h = ht + (int64_t)row * d;
+
+  // ||h||_2 in float64
+  double hn = 0.0;
+  for (int j = tid; j < d; j += SEL_THREADS) {
+    const double x = (double)to_f32<T>(h[j]);
+    hn += x * x;
+  }
+  hn = sqrt(block_sum_256(hn, shd));
+  const double eps = 2.0 * (double)d * 0x1p-23 * hn * (*wmax);
+
+  // pass 1: top 12 bits of the key
+  for (int b = tid; b < 4096; b += SEL_THREADS) hist[b] = 0u;
+  __syncthreads();
+  for (int v = tid; v < V; v += SEL_THREADS) atomicAdd(&hist[float_key(s[v]) >> 20], 1u);
+  __syncthreads();
+  select_bin(hist, K, sh, sh + 34);
+  const uint32_t B = (uint32_t)sh[34];
+  const int above = sh[35];
+  __syncthreads();
+  // pass 2: next 12 bits inside bin B
+  for (int b = tid; b < 4096; b += SEL_THREADS) hist[b] = 0u;
+  __syncthreads();
+  for (int v = tid; v < V; v += SEL_THREADS) {
+    const uint32_t key = float_key(s[v]);
+    if ((key >> 20) == B) atomicAdd(&hist[(key >> 8) & 0xfffu], 1u);
+  }
+  __syncthreads();
+  select_bin(hist, K - above, sh, sh + 36);
+  const uint32_t B2 = (uint32_t)sh[36];
+  const float lo = key_float((B << 20) | (B2 << 8));
+  const float thr = __double2float_rd((double)lo - 2.0 * eps);
+  if (tid == 0) sh[38] = 0;
+  __syncthreads();
+  // pass 3: candidates
+  for (int v = tid; v < V; v += SEL_THREADS) {
+    if (s[v] >= thr) {
+      const int pos = atomicAdd(&sh[38], 1);
+      if (pos < SEL_CAP) cidx[pos] = v;
+    }
+  }
+  __syncthreads();
+  const int C = sh[38];
+  if (C > SEL_CAP) {
+    for (int k = tid; k < K; k += SEL_THREADS) {
+      idx_out[(int64_t)row * K + k] = -1;
+      val_out[(int64_t)row * K + k] = from_f32<VT>(NAN);
+    }
+    if (tid == 0) atomicAdd(overflow, 1);
+    return;
+  }
+  // float64 re-scoring: one wave per candidate, lanes split d in 16-byte chunks
+  constexpr int EPC = 16 / int(sizeof(T));
+  for (int c = wave; c < C; c += SEL_THREADS / 64) {
+    const T* w = wt + (int64_t)cidx[c] * d;
+    double acc = 0.0;
+    for (int j = lane * EPC; j < d; j += 64 * EPC) {
+      const u32x4 hv = *(const u32x4*)(h + j);
+      const u32x4 wv = *(const u32x4*)(w + j);
+      const T* hp = (const T*)&hv;
+      const T* wp = (const T*)&wv;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc = fma((double)to_f32<T>(hp[e]), (double)to_f32<T>(wp[e]), acc);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) cscore[c] = acc;
+  }
+  __syncthreads();
+  // rank by (score desc, index asc); write the first K
+  for (int c = tid; c < C; c += SEL_THREADS) {
+    const double sc = cscore[c];
+    const int vi = cidx[c];
+    int rank = 0;
+    for (int o = 0; o < C; ++o) {
+      const double so = cscore[o];
+      rank += (so > sc) || (so == sc && cidx[o] < vi);
+    }
+    if (rank < K) {
+      idx_out[(int64_t)row * K + rank] = vi;
+      if constexpr (sizeof(VT) == 2) val_out[(int64_t)row * K + rank] = f64_to_bf16_rne(sc);
+      else val_out[(int64_t)row * K + rank] = (float)sc;
+    }
+  }
+}
+
+}  // namespace kd

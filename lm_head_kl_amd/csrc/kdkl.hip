@@ -1,0 +1,427 @@
+// Host side of the kdkl C ABI: argument validation, workspace planning and the
+// launch sequences of the teacher-cache build and the chunked KL forward/backward.
+// The declarations and the contract of every entry point are in include/kdkl.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
+#include "kdkl.h"
+#include "kd_aux.hpp"
+#include "kd_gemm.hpp"
+
+using namespace kd;
+
+namespace {
+
+constexpr int64_t kMaxVocab = 4194304;   // 16384 vocabulary tiles (bucket histogram in LDS)
+constexpr int kMaxK = 65535;             // k fits the 16-bit field of a bucket entry
+constexpr int kMaxKTopk = 4096;          // selection candidates are held in LDS
+constexpr int64_t kDefaultChunkKL = 16384;
+constexpr int64_t kDefaultChunkTopk = 8192;
+constexpr int kGroup = 8;
+
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  int64_t N, d, V;
+  int K;
+  float tau;
+  kd_dtype xdt, vdt, dhdt;
+  int64_t esz;      // bytes per H/W element
+  int64_t Nc;       // tokens per chunk (multiple of 256)
+  int64_t V_pad;    // vocabulary rounded up to 64 (K-extent of dH)
+  int n_ty;         // 256-wide vocabulary tiles
+};
+
+// Workspace regions, each 256-byte aligned, in bytes from the workspace start.
+struct Layout {
+  size_t entries, offsets, zg, partials, block_sums, flags;       // forward
+  size_t wt, ht, dz, dzt;                                         // backward
+  size_t s, bmax, wmax, overflow;                                 // cache build
+  size_t total;
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t lim = INT64_MAX / 4) { return a == 0 || b <= lim / a; }
+
+kd_status validate(kd_op op, const kd_problem* p, Plan* pl) {
+  if (!p) return KD_ERR_NULL_POINTER;
+  if (p->x_dtype != KD_F32 && p->x_dtype != KD_BF16) return KD_ERR_BAD_DTYPE;
+  if (p->val_dtype != KD_F32 && p->val_dtype != KD_BF16) return KD_ERR_BAD_DTYPE;
+  if (p->x_dtype == KD_BF16 && p->val_dtype != KD_BF16) return KD_ERR_BAD_DTYPE;
+  if (p->x_dtype == KD_F32 && p->val_dtype != KD_F32) return KD_ERR_BAD_DTYPE;
+  if (op == KD_OP_KL_BWD && p->dh_dtype != KD_F32 && p->dh_dtype != KD_BF16) return KD_ERR_BAD_DTYPE;
+  if (p->n_tokens < 0 || p->d_model < 8 || (p->d_model % 8) != 0) return KD_ERR_BAD_SHAPE;
+  if (p->vocab < 1 || p->vocab > kMaxVocab) return KD_ERR_BAD_SHAPE;
+  if (p->k < 1 || p->k > kMaxK || p->k > p->vocab) return KD_ERR_BAD_SHAPE;
+  if (op == KD_OP_TOPK_BUILD && p->k > kMaxKTopk) return KD_ERR_BAD_SHAPE;
+  if (p->chunk_tokens < 0) return KD_ERR_BAD_SHAPE;
+  if (p->d_model > (1 << 20) || p->n_tokens > (int64_t(1) << 31) - 256) return KD_ERR_BAD_SHAPE;
+  if (!mul_ok(p->n_tokens, p->k) || !mul_ok(p->n_tokens, p->d_model) || !mul_ok(p->vocab, p->d_model))
+    return KD_ERR_BAD_SHAPE;
+  if (op != KD_OP_TOPK_BUILD && !(std::isfinite(p->tau) && p->tau > 0.f)) return KD_ERR_BAD_TAU;
+  pl->N = p->n_tokens;
+  pl->d = p->d_model;
+  pl->V = p->vocab;
+  pl->K = p->k;
+  pl->tau = p->tau;
+  pl->xdt = (kd_dtype)p->x_dtype;
+  pl->vdt = (kd_dtype)p->val_dtype;
+  pl->dhdt = (kd_dtype)p->dh_dtype;
+  pl->esz = p->x_dtype == KD_BF16 ? 2 : 4;
+  const int64_t def = op == KD_OP_TOPK_BUILD ? kDefaultChunkTopk : kDefaultChunkKL;
+  int64_t c = p->chunk_tokens > 0 ? p->chunk_tokens : def;
+  c = round_up(c, BX);
+  c = std::min<int64_t>(c, round_up(std::max<int64_t>(pl->N, 1), BX));
+  pl->Nc = c;
+  pl->V_pad = round_up(pl->V, 64);
+  pl->n_ty = (int)cdiv(pl->V, BY);
+  // 32-bit offsets inside one 256-row tile of every GEMM operand
+  if (!mul_ok(BX, std::max<int64_t>(pl->V_pad, pl->d) + 64, INT32_MAX)) return KD_ERR_BAD_SHAPE;
+  if (!mul_ok(pl->Nc, pl->V_pad) || !mul_ok(pl->d, pl->V_pad)) return KD_ERR_BAD_SHAPE;
+  return KD_OK;
+}
+
+size_t layout(kd_op op, const Plan& pl, Layout* L) {
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = (size_t)round_up((int64_t)(cur + bytes), 256);
+    return at;
+  };
+  std::memset(L, 0, sizeof(*L));
+  const int64_t n_tx = pl.Nc / BX;
+  if (op == KD_OP_KL_FWD) {
+    L->entries = take(sizeof(uint32_t) * pl.Nc * pl.K);
+    L->offsets = take(sizeof(int) * n_tx * (pl.n_ty + 1));
+    L->zg = take(sizeof(float) * pl.Nc * pl.K);
+    L->partials = take(sizeof(float2) * pl.n_ty * pl.Nc);
+    L->block_sums = take(sizeof(double) * (size_t)std::max<int64_t>(1, cdiv(pl.N, 256)));
+    L->flags = take(sizeof(int) * 4);
+  } else if (op == KD_OP_KL_BWD) {
+    L->wt = take((size_t)(pl.esz * pl.d * pl.V_pad));
+    L->ht = take((size_t)(pl.esz * pl.d * pl.Nc));
+    L->dz = take((size_t)(pl.esz * pl.Nc * pl.V_pad));
+    L->dzt = take((size_t)(pl.esz * pl.V_pad * pl.Nc));
+  } else {
+    L->s = take(sizeof(float) * (size_t)(pl.Nc * pl.V_pad));
+    L->bmax = take(sizeof(double) * 1024);
+    L->wmax = take(sizeof(double));
+    L->overflow = take(sizeof(int) * 4);
+  }
+  L->total = cur;
+  return cur;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+kd_status check_device() {
+  static int state[256];   // 0 unknown, 1 gfx950, 2 other
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KD_ERR_NO_DEVICE;
+  if (dev < 256 && state[dev]) return state[dev] == 1 ? KD_OK : KD_ERR_UNSUPPORTED_ARCH;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KD_ERR_NO_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 256) state[dev] = ok ? 1 : 2;
+  return ok ? KD_OK : KD_ERR_UNSUPPORTED_ARCH;
+}
+
+bool debug_checks() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = std::getenv("KD_CHECK");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+inline kd_status launched() { return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH; }
+
+#define KD_TRY(x)                 \
+  do {                            \
+    const kd_status _s = (x);     \
+    if (_s != KD_OK) return _s;   \
+  } while (0)
+
+GemmArgs gemm_args(const void* X, int64_t ldx, int nx, const void* Y, int64_t ldy, int ny, int k) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.X = X;
+  g.ldx = ldx;
+  g.nx = nx;
+  g.Y = Y;
+  g.ldy = ldy;
+  g.ny = ny;
+  g.k = k;
+  g.n_tx = (int)cdiv(nx, BX);
+  g.n_ty = (int)cdiv(ny, BY);
+  g.group = kGroup;
+  return g;
+}
+
+template <typename T, int EPI>
+kd_status run_gemm(const GemmArgs& g, hipStream_t st) {
+  if (g.nx <= 0 || g.ny <= 0) return KD_OK;
+  const unsigned blocks = (unsigned)(g.n_tx * g.n_ty);
+  hipLaunchKernelGGL((gemm_kernel<T, EPI>), dim3(blocks), dim3(NTHREADS), 0, st, g);
+  return launched();
+}
+
+template <typename T>
+kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
+                   const void* val, float* loss, float* lse, float* kl_rows, char* ws, hipStream_t st) {
+  uint32_t* entries = (uint32_t*)(ws + L.entries);
+  int* offsets = (int*)(ws + L.offsets);
+  float* zg = (float*)(ws + L.zg);
+  float2* partials = (float2*)(ws + L.partials);
+  double* bsums = (double*)(ws + L.block_sums);
+  int* flags = (int*)(ws + L.flags);
+  const bool check = debug_checks();
+  if (check) {
+    if (hipMemsetAsync(flags, 0, sizeof(int) * 4, st) != hipSuccess) return KD_ERR_LAUNCH;
+  }
+  const float inv_tau = 1.0f / pl.tau;
+  for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
+    const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
+    const int n_tx = (int)cdiv(nr, BX);
+    const int32_t* idx_c = idx + r0 * pl.K;
+    const size_t hist_bytes = sizeof(int) * (pl.n_ty + 64);
+    hipLaunchKernelGGL(bucket_kernel, dim3(n_tx), dim3(1024), hist_bytes, st, idx_c, nr, pl.K, (int)pl.V, pl.n_ty,
+                       entries, offsets, flags);
+    KD_TRY(launched());
+    GemmArgs g = gemm_args((const T*)h + r0 * pl.d, pl.d, nr, w, pl.d, (int)pl.V, (int)pl.d);
+    g.entries = entries;
+    g.offsets = offsets;
+    g.kc = pl.K;
+    g.zg = zg;
+    g.partials = partials;
+    g.ld_part = pl.Nc;
+    KD_TRY((run_gemm<T, EPI_KL_FWD>(g, st)));
+    const int nb = (int)cdiv(nr, 256);
+    if (pl.vdt == KD_BF16)
+      hipLaunchKernelGGL(merge_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty, idx_c,
+                         (const bf16_t*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
+                         kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / 256);
+    else
+      hipLaunchKernelGGL(merge_kernel<float>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty, idx_c,
+                         (const float*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
+                         kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / 256);
+    KD_TRY(launched());
+  }
+  const int nb_all = (int)cdiv(pl.N, 256);
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsums, nb_all,
+                     pl.N > 0 ? 1.0 / (double)pl.N : 0.0, loss);
+  KD_TRY(launched());
+  if (check) {
+    int bad = 0;
+    if (hipMemcpyAsync(&bad, flags, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return KD_ERR_LAUNCH;
+    if (hipStreamSynchronize(st) != hipSuccess) return KD_ERR_LAUNCH;
+    if (bad) return KD_ERR_IDX_OUT_OF_RANGE;
+  }
+  return KD_OK;
+}
+
+template <typename T>
+kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
+                   const void* val, const float* lse, const float* grad, void* dh, float* dw, char* ws,
+                   hipStream_t st) {
+  if (pl.N == 0) {
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(1024), dim3(256), 0, st, dw, pl.V * pl.d, 0.0f);
+    return launched();
+  }
+  T* wt = (T*)(ws + L.wt);
+  T* ht = (T*)(ws + L.ht);
+  T* dz = (T*)(ws + L.dz);
+  T* dzt = (T*)(ws + L.dzt);
+  const float inv_n = 1.0f / (float)pl.N;
+  const float inv_tau = 1.0f / pl.tau;
+  // W^T [d][V_pad], zero past V
+  hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(pl.V_pad, 64), (unsigned)cdiv(pl.d, 64)),
+                     dim3(256), 0, st, (const T*)w, pl.d, (int)pl.V, (int)pl.d, wt, pl.V_pad, (int)pl.V_pad);
+  KD_TRY(launched());
+  for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
+    const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
+    const int nr64 = (int)round_up(nr, 64);
+    const T* hc = (const T*)h + r0 * pl.d;
+    // H^T [d][Nc], zero past nr
+    hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(nr64, 64), (unsigned)cdiv(pl.d, 64)), dim3(256),
+                       0, st, hc, pl.d, nr, (int)pl.d, ht, pl.Nc, nr64);
+    KD_TRY(launched());
+    // recompute logits, dZ = (g/N) softmax
+    GemmArgs g = gemm_args(hc, pl.d, nr, w, pl.d, (int)pl.V, (int)pl.d);
+    g.out = dz;
+    g.ldo = pl.V_pad;
+    g.out2 = dzt;
+    g.ldo2 = pl.Nc;
+    g.out_rows = nr64;
+    g.out_cols = (int)pl.V_pad;
+    g.lse = lse + r0;
+    g.grad = grad;
+    g.inv_n = inv_n;
+    KD_TRY((run_gemm<T, EPI_KL_DZ>(g, st)));
+    // subtract the teacher at the cached entries
+    const int nb = (int)cdiv(nr, 256);
+    if (pl.vdt == KD_BF16)
+      hipLaunchKernelGGL((scatter_kernel<T, bf16_t>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
+                         (const bf16_t*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.V_pad, dzt,
+                         pl.Nc);
+    else
+      hipLaunchKernelGGL((scatter_kernel<T, float>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
+                         (const float*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.V_pad, dzt,
+                         pl.Nc);
+    KD_TRY(launched());
+    // dH = dZ W  (P[t][j] = sum_v dZ[t][v] W^T[j][v])
+    GemmArgs gh = gemm_args(dz, pl.V_pad, nr, wt, pl.V_pad, (int)pl.d, (int)pl.V_pad);
+    gh.out_rows = nr;
+    gh.out_cols = (int)pl.d;
+    gh.ldo = pl.d;
+    if (pl.dhdt == KD_F32) {
+      gh.out = (float*)dh + r0 * pl.d;
+      KD_TRY((run_gemm<T, EPI_STORE_F32>(gh, st)));
+    } else {
+      gh.out = (bf16_t*)dh + r0 * pl.d;
+      KD_TRY((run_gemm<T, EPI_STORE_BF16>(gh, st)));
+    }
+    // dW (+)= dZ^T H  (P[v][j] = sum_t dZ^T[v][t] H^T[j][t])
+    GemmArgs gw = gemm_args(dzt, pl.Nc, (int)pl.V, ht, pl.Nc, (int)pl.d, nr64);
+    gw.out = dw;
+    gw.ldo = pl.d;
+    gw.out_rows = (int)pl.V;
+    gw.out_cols = (int)pl.d;
+    gw.accumulate = r0 > 0;
+    KD_TRY((run_gemm<T, EPI_STORE_F32>(gw, st)));
+  }
+  return KD_OK;
+}
+
+template <typename T, typename VT>
+kd_status topk_impl(const Plan& pl, const Layout& L, const void* ht, const void* wt, int32_t* idx, void* val,
+                    char* ws, hipStream_t st) {
+  if (pl.N == 0) return KD_OK;
+  float* S = (float*)(ws + L.s);
+  double* bmax = (double*)(ws + L.bmax);
+  double* wmax = (double*)(ws + L.wmax);
+  int* overflow = (int*)(ws + L.overflow);
+  const bool check = debug_checks();
+  if (check && hipMemsetAsync(overflow, 0, sizeof(int) * 4, st) != hipSuccess) return KD_ERR_LAUNCH;
+  const int nblk = (int)std::min<int64_t>(1024, cdiv(pl.V, 4));
+  hipLaunchKernelGGL(rownorm_max_kernel<T>, dim3(nblk), dim3(256), 0, st, (const T*)wt, (int)pl.V, (int)pl.d, bmax);
+  KD_TRY(launched());
+  hipLaunchKernelGGL(max_reduce_kernel, dim3(1), dim3(256), 0, st, bmax, nblk, wmax);
+  KD_TRY(launched());
+  for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
+    const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
+    const T* hc = (const T*)ht + r0 * pl.d;
+    GemmArgs g = gemm_args(hc, pl.d, nr, wt, pl.d, (int)pl.V, (int)pl.d);
+    g.out = S;
+    g.ldo = pl.V_pad;
+    g.out_rows = nr;
+    g.out_cols = (int)pl.V_pad;
+    KD_TRY((run_gemm<T, EPI_STORE_F32>(g, st)));
+    hipLaunchKernelGGL((topk_select_kernel<T, VT>), dim3(nr), dim3(SEL_THREADS), 0, st, S, pl.V_pad, (int)pl.V,
+                       pl.K, hc, (int)pl.d, (const T*)wt, wmax, idx + r0 * pl.K, (VT*)val + r0 * pl.K, overflow);
+    KD_TRY(launched());
+  }
+  if (check) {
+    int ov = 0;
+    if (hipMemcpyAsync(&ov, overflow, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return KD_ERR_LAUNCH;
+    if (hipStreamSynchronize(st) != hipSuccess) return KD_ERR_LAUNCH;
+    if (ov) return KD_ERR_TOPK_OVERFLOW;
+  }
+  return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_workspace_size(kd_op op, const kd_problem* p, size_t* bytes) {
+  if (!bytes) return KD_ERR_NULL_POINTER;
+  if (op != KD_OP_TOPK_BUILD && op != KD_OP_KL_FWD && op != KD_OP_KL_BWD) return KD_ERR_BAD_SHAPE;
+  Plan pl;
+  KD_TRY(validate(op, p, &pl));
+  Layout L;
+  *bytes = layout(op, pl, &L);
+  return KD_OK;
+}
+
+kd_status kd_topk_cache_build(const kd_problem* p, const void* h_t, const void* w_t, int32_t* idx_out,
+                              void* val_out, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  KD_TRY(validate(KD_OP_TOPK_BUILD, p, &pl));
+  if (pl.N > 0 && (!h_t || !idx_out || !val_out)) return KD_ERR_NULL_POINTER;
+  if (!w_t || !ws) return KD_ERR_NULL_POINTER;
+  if (!aligned16(h_t) || !aligned16(w_t) || !aligned16(idx_out) || !aligned16(val_out) || !aligned16(ws))
+    return KD_ERR_MISALIGNED;
+  Layout L;
+  if (ws_bytes < layout(KD_OP_TOPK_BUILD, pl, &L)) return KD_ERR_WORKSPACE_TOO_SMALL;
+  KD_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (pl.xdt == KD_BF16) return topk_impl<bf16_t, bf16_t>(pl, L, h_t, w_t, idx_out, val_out, (char*)ws, st);
+  return topk_impl<float, float>(pl, L, h_t, w_t, idx_out, val_out, (char*)ws, st);
+}
+
+kd_status kd_chunked_kl_fwd(const kd_problem* p, const void* h, const void* w, const int32_t* idx,
+                            const void* val, float* loss_out, float* lse_out, float* kl_rows_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  Plan pl;
+  KD_TRY(validate(KD_OP_KL_FWD, p, &pl));
+  if (!w || !loss_out || !ws) return KD_ERR_NULL_POINTER;
+  if (pl.N > 0 && (!h || !idx || !val || !lse_out)) return KD_ERR_NULL_POINTER;
+  if (!aligned16(h) || !aligned16(w) || !aligned16(idx) || !aligned16(val) || !aligned16(loss_out) ||
+      !aligned16(lse_out) || !aligned16(kl_rows_out) || !aligned16(ws))
+    return KD_ERR_MISALIGNED;
+  Layout L;
+  if (ws_bytes < layout(KD_OP_KL_FWD, pl, &L)) return KD_ERR_WORKSPACE_TOO_SMALL;
+  KD_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (pl.xdt == KD_BF16)
+    return fwd_impl<bf16_t>(pl, L, h, w, idx, val, loss_out, lse_out, kl_rows_out, (char*)ws, st);
+  return fwd_impl<float>(pl, L, h, w, idx, val, loss_out, lse_out, kl_rows_out, (char*)ws, st);
+}
+
+kd_status kd_chunked_kl_bwd(const kd_problem* p, const void* h, const void* w, const int32_t* idx,
+                            const void* val, const float* lse, const float* grad_loss, void* dh_out, float* dw_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  KD_TRY(validate(KD_OP_KL_BWD, p, &pl));
+  if (!w || !dw_out || !ws) return KD_ERR_NULL_POINTER;
+  if (pl.N > 0 && (!h || !idx || !val || !lse || !dh_out)) return KD_ERR_NULL_POINTER;
+  if (!aligned16(h) || !aligned16(w) || !aligned16(idx) || !aligned16(val) || !aligned16(lse) ||
+      !aligned16(dh_out) || !aligned16(dw_out) || !aligned16(ws))
+    return KD_ERR_MISALIGNED;
+  Layout L;
+  if (ws_bytes < layout(KD_OP_KL_BWD, pl, &L)) return KD_ERR_WORKSPACE_TOO_SMALL;
+  KD_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (pl.xdt == KD_BF16)
+    return bwd_impl<bf16_t>(pl, L, h, w, idx, val, lse, grad_loss, dh_out, dw_out, (char*)ws, st);
+  return bwd_impl<float>(pl, L, h, w, idx, val, lse, grad_loss, dh_out, dw_out, (char*)ws, st);
+}
+
+const char* kd_status_string(kd_status s) {
+  switch (s) {
+    case KD_OK: return "ok";
+    case KD_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case KD_ERR_BAD_SHAPE: return "a size is outside the supported domain";
+    case KD_ERR_BAD_DTYPE: return "unsupported dtype or dtype combination";
+    case KD_ERR_BAD_TAU: return "tau must be finite and > 0";
+    case KD_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+    case KD_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than kd_workspace_size()";
+    case KD_ERR_NO_DEVICE: return "no HIP device is current";
+    case KD_ERR_UNSUPPORTED_ARCH: return "the current device is not gfx950 (MI355X)";
+    case KD_ERR_LAUNCH: return "a kernel launch failed";
+    case KD_ERR_IDX_OUT_OF_RANGE: return "a cached index is outside [0, V)";
+    case KD_ERR_TOPK_OVERFLOW: return "too many near-ties at the K-th teacher logit";
+  }
+  return "unknown status";
+}
+
+int kd_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Inputs are seeded and synthetic (``kd_synth``); the teacher cache fed to the
+loss is the oracle's exact top-K, so both sides see the same cache bytes.
+Sizes here are small enough for the oracle to finish in seconds while still
+spanning several 256 x 256 tiles and ragged tails in every dimension.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kd_synth
+import lm_head_kl_amd as kd
+import oracle
+from gpu_util import (GRAD_TOL, LOSS_RTOL, LSE_RTOL, bf16_bits_of, device, rel_max_err, to_dev, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+# (N, d, V, K, dtype, tau): ragged N, d not a multiple of the 64-wide K stage,
+# vocabularies that end inside a 256-wide tile.
+SHAPES = [
+    (300, 136, 1000, 7, "bf16", 1.0),
+    (520, 264, 1300, 33, "bf16", 2.0),
+    (64, 64, 300, 1, "bf16", 0.5),
+    (700, 128, 2600, 100, "f32", 1.5),
+    (257, 512, 4099, 64, "bf16", 1.0),
+]
+
+
+def _problem(n, d, v, k, dtype, seed=0):
+    p = kd_synth.small_problem(n, d, v, seed=seed, dtype=dtype)
+    H = kd_synth.to_float64(p["H"], dtype)
+    W = kd_synth.to_float64(p["W"], dtype)
+    WT = kd_synth.to_float64(p["WT"], dtype)
+    idx, val, _ = oracle.topk_cache(H, WT, k, "bf16" if dtype == "bf16" else "f32")
+    return p, H, W, WT, idx, val
+
+
+def _val64(val, dtype):
+    return kd_synth.to_float64(val, "bf16" if dtype == "bf16" else "f32")
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("chunk", [0, 256])
+def test_forward_backward_match_oracle(shape, chunk):
+    n, d, v, k, dtype, tau = shape
+    p, H, W, WT, idx, val = _problem(n, d, v, k, dtype)
+    ref_loss, ref_lse, ref_rows = oracle.kl_forward(H, W, idx, _val64(val, dtype), tau)
+    g = 0.37
+    ref_dH, ref_dW = oracle.kl_backward(H, W, idx, _val64(val, dtype), tau, grad=g)
+
+    h, w = to_dev(p["H"], dtype), to_dev(p["W"], dtype)
+    ti = torch.from_numpy(idx).to(device())
+    tv = to_dev(val, dtype)
+    loss, lse, rows = kd.kd_chunked_kl_fwd(h, w, ti, tv, tau, with_rows=True, chunk_tokens=chunk)
+    gt = torch.tensor(g, dtype=torch.float32, device=device())
+    dh, dw = kd.kd_chunked_kl_bwd(h, w, ti, tv, tau, lse, gt, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+
+    assert abs(loss.item() - ref_loss) <= LOSS_RTOL * abs(ref_loss)
+    np.testing.assert_allclose(to_f64(lse), ref_lse, rtol=LSE_RTOL)
+    np.testing.assert_allclose(to_f64(rows), ref_rows, rtol=5e-3, atol=5e-3)
+    assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL
+    assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_topk_cache_bit_exact(shape):
+    n, d, v, k, dtype, _ = shape
+    p, H, W, WT, idx, val = _problem(n, d, v, k, dtype)
+    gi, gv = kd.kd_topk_cache_build(to_dev(p["H"], dtype), to_dev(p["WT"], dtype), k, chunk_tokens=256)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gi.cpu().numpy(), idx)
+    if dtype == "bf16":
+        np.testing.assert_array_equal(bf16_bits_of(gv), val)
+    else:
+        np.testing.assert_array_equal(gv.cpu().numpy().view(np.uint32), val.view(np.uint32))
+
+
+def _tiny_config():
+    w = kd_synth.WORKLOADS["tiny_fp32"]
+    H = kd_synth.hidden(w, w.tokens[0])
+    W = kd_synth.student_head(w)
+    WT = kd_synth.teacher_head(w)
+    return w, H, W, WT
+
+
+@pytest.mark.parametrize("k", [16, 4096])
+def test_tiny_fp32_workload(k):
+    """256 tokens, d=256, V=4096, tau=1, float32; K=16 and the full-vocabulary
+    cache (K=|V|: the full KL)."""
+    w, H, W, WT = _tiny_config()
+    idx, val, _ = oracle.topk_cache(H, WT, k, "f32")
+    ref_loss, ref_lse, _ = oracle.kl_forward(H, W, idx, val.astype(np.float64), 1.0)
+    ref_dH, ref_dW = oracle.kl_backward(H, W, idx, val.astype(np.float64), 1.0)
+    h, wd = to_dev(H, "f32"), to_dev(W, "f32")
+    gi, gv = kd.kd_topk_cache_build(h, to_dev(WT, "f32"), k)
+    loss, lse, _ = kd.kd_chunked_kl_fwd(h, wd, gi, gv, 1.0)
+    dh, dw = kd.kd_chunked_kl_bwd(h, wd, gi, gv, 1.0, lse)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gi.cpu().numpy(), idx)
+    np.testing.assert_array_equal(gv.cpu().numpy().view(np.uint32), val.view(np.uint32))
+    assert abs(loss.item() - ref_loss) <= LOSS_RTOL * abs(ref_loss)
+    np.testing.assert_allclose(to_f64(lse), ref_lse, rtol=LSE_RTOL)
+    assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL
+    assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+
+
+def test_deterministic_and_invariants():
+    n, d, v, k, dtype, tau = 700, 256, 3000, 20, "bf16", 1.0
+    p, H, W, WT, idx, val = _problem(n, d, v, k, dtype, seed=3)
+    h, w = to_dev(p["H"], dtype), to_dev(p["W"], dtype)
+    ti, tv = torch.from_numpy(idx).to(device()), to_dev(val, dtype)
+    outs = []
+    for _ in range(2):
+        loss, lse, rows = kd.kd_chunked_kl_fwd(h, w, ti, tv, tau, with_rows=True, chunk_tokens=256)
+        dh, dw = kd.kd_chunked_kl_bwd(h, w, ti, tv, tau, lse, chunk_tokens=256)
+        outs.append([x.clone() for x in (loss, lse, rows, dh, dw)])
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    loss, lse, rows, dh, dw = outs[0]
+    assert (rows >= -1e-4).all()
+    assert abs(rows.double().mean().item() - loss.item()) <= 1e-5 * abs(loss.item())
+    # sum over the vocabulary of dW vanishes (each dZ row sums to zero)
+    colsum = dw.double().sum(0).abs().max().item()
+    assert colsum <= 1e-3 * dw.double().abs().max().item() * 50
+
+
+def test_empty_and_single_entry():
+    n, d, v = 0, 64, 500
+    h = torch.zeros((0, d), dtype=torch.bfloat16, device=device())
+    w = torch.randn((v, d), device=device()).to(torch.bfloat16)
+    ti = torch.zeros((0, 3), dtype=torch.int32, device=device())
+    tv = torch.zeros((0, 3), dtype=torch.bfloat16, device=device())
+    loss, lse, _ = kd.kd_chunked_kl_fwd(h, w, ti, tv, 1.0)
+    dh, dw = kd.kd_chunked_kl_bwd(h, w, ti, tv, 1.0, lse)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and dh.numel() == 0 and float(dw.abs().max()) == 0.0
+    # K = 1 is the cross-entropy with the cached index as label
+    p = kd_synth.small_problem(200, 64, 700, seed=5)
+    H = kd_synth.to_float64(p["H"], "bf16")
+    W = kd_synth.to_float64(p["W"], "bf16")
+    idx = np.random.default_rng(0).integers(0, 700, size=(200, 1)).astype(np.int32)
+    val = np.zeros((200, 1), dtype=np.uint16)
+    ce = torch.nn.functional.cross_entropy(torch.tensor(H @ W.T), torch.tensor(idx[:, 0]).long()).item()
+    loss, _, _ = kd.kd_chunked_kl_fwd(to_dev(p["H"], "bf16"), to_dev(p["W"], "bf16"),
+                                      torch.from_numpy(idx).to(device()), to_dev(val, "bf16"), 1.0)
+    assert abs(loss.item() - ce) <= LOSS_RTOL * ce
+
+
+def test_out_of_range_index_gives_nan_row_not_a_fault():
+    p = kd_synth.small_problem(300, 64, 600, seed=6)
+    idx = np.random.default_rng(1).integers(0, 600, size=(300, 5)).astype(np.int32)
+    idx[17, 2] = 600
+    idx[200, 0] = -3
+    val = np.zeros((300, 5), dtype=np.uint16)
+    loss, lse, rows = kd.kd_chunked_kl_fwd(to_dev(p["H"], "bf16"), to_dev(p["W"], "bf16"),
+                                           torch.from_numpy(idx).to(device()), to_dev(val, "bf16"), 1.0,
+                                           with_rows=True)
+    torch.cuda.synchronize()
+    r = rows.cpu().numpy()
+    assert np.isnan(r[17]) and np.isnan(r[200]) and np.isfinite(np.delete(r, [17, 200])).all()
+    assert np.isnan(loss.item())
+
+
+def test_repeated_indices_scatter_add():
+    n, d, v, k = 260, 64, 300, 6
+    p = kd_synth.small_problem(n, d, v, seed=8)
+    H = kd_synth.to_float64(p["H"], "bf16")
+    W = kd_synth.to_float64(p["W"], "bf16")
+    idx, valb = kd_synth.random_cache(n, v, k, seed=2, distinct=False)
+    val = kd_synth.to_float64(valb, "bf16")
+    ref_dH, ref_dW = oracle.kl_backward(H, W, idx, val, 1.0)
+    ref_loss, _, _ = oracle.kl_forward(H, W, idx, val, 1.0)
+    h, w = to_dev(p["H"], "bf16"), to_dev(p["W"], "bf16")
+    ti, tv = torch.from_numpy(idx).to(device()), to_dev(valb, "bf16")
+    loss, lse, _ = kd.kd_chunked_kl_fwd(h, w, ti, tv, 1.0)
+    dh, dw = kd.kd_chunked_kl_bwd(h, w, ti, tv, 1.0, lse)
+    torch.cuda.synchronize()
+    assert abs(loss.item() - ref_loss) <= LOSS_RTOL * abs(ref_loss)
+    assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL
+    assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+
+
+def test_autograd_function():
+    n, d, v, k = 300, 128, 900, 10
+    p, H, W, WT, idx, val = _problem(n, d, v, k, "f32", seed=9)
+    ref_dH, ref_dW = oracle.kl_backward(H, W, idx, val.astype(np.float64), 1.0, grad=2.0)
+    h = to_dev(p["H"], "f32").requires_grad_(True)
+    w = to_dev(p["W"], "f32").requires_grad_(True)
+    loss = kd.chunked_kl_loss(h, w, torch.from_numpy(idx).to(device()), to_dev(val, "f32"), 1.0)
+    (2.0 * loss).backward()
+    torch.cuda.synchronize()
+    assert rel_max_err(to_f64(h.grad), ref_dH) <= GRAD_TOL
+    assert rel_max_err(to_f64(w.grad), ref_dW) <= GRAD_TOL

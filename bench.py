@@ -1,0 +1,222 @@
+#!/usr/bin/env python
+"""Throughput of the fused, chunked top-K KL loss (forward + backward) on one MI355X.
+
+A step is one forward (``kd_chunked_kl_fwd``) and one backward
+(``kd_chunked_kl_bwd``) pass over one batch of synthetic tokens: logits
+recomputed tile by tile in both passes, online log-sum-exp, cached-entry
+gather, dZ, dH and dW.  The teacher cache is built once beforehand with
+``kd_topk_cache_build`` (the offline pass) and timed separately.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused LM-head+top-K KL fwd+bwd tokens/s (V=128256,d=4096); MFMA util; peak GB"
+BF16_DENSE_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP32_DENSE_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("lm_head_kl_amd/csrc/kd_gemm.hpp", "lm_head_kl_amd/csrc/kd_common.hpp")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kind: str):
+    """HBM bytes per launch of `kind` from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kind)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(workload, n_rows: int, k: int):
+    """The float64 oracle, as it stands, on the first ``n_rows`` tokens of the same
+    workload (full vocabulary and hidden size) with a synthetic cache of the same
+    shape; returns tokens/s of its forward + backward."""
+    import numpy as np
+    import kd_synth
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    H = kd_synth.to_float64(kd_synth.hidden(workload, n_rows), workload.dtype)
+    W = kd_synth.to_float64(kd_synth.student_head(workload), workload.dtype)
+    idx, valb = kd_synth.random_cache(n_rows, workload.vocab, k, seed=5, val_dtype=workload.val_dtype)
+    val = kd_synth.to_float64(valb, workload.val_dtype)
+    t0 = time.perf_counter()
+    oracle.kl_forward(H, W, idx, val, workload.tau)
+    oracle.kl_backward(H, W, idx, val, workload.tau)
+    dt = time.perf_counter() - t0
+    return {"value": n_rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_rows} tokens of the workload (full V={workload.vocab}, d={workload.d}, K={k}), "
+                      f"float64 forward+backward, synthetic cache of the same shape; {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="packed131k_v128k")
+    ap.add_argument("--tokens", type=int, default=0, help="override N (e.g. a sweep point)")
+    ap.add_argument("--k", type=int, default=0, help="override K")
+    ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library default)")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache-build-timing", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the loss would shard over tokens with one dW all-reduce; see the design notes).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import kd_synth
+    import lm_head_kl_amd as kd
+
+    kd.load_library()
+    dev = torch.device("cuda:0")
+    w = kd_synth.WORKLOADS[args.workload]
+    n = args.tokens or w.tokens[0]
+    k = args.k or (100 if 100 in w.ks else w.ks[0])
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def to_dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    t0 = time.perf_counter()
+    h = to_dev(kd_synth.hidden(w, n))
+    wd = to_dev(kd_synth.student_head(w))
+    wt = to_dev(kd_synth.teacher_head(w))
+    torch.cuda.synchronize()
+    log(f"{args.workload}: N={n} d={w.d} V={w.vocab} K={k} tau={w.tau} {w.dtype}; inputs in "
+        f"{time.perf_counter() - t0:.1f}s")
+
+    # offline teacher cache (H_T = H: the synthetic teacher shares the hidden states)
+    idx, val = kd.kd_topk_cache_build(h, wt, k)
+    torch.cuda.synchronize()
+    cache = None
+    if not args.no_cache_build_timing:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        idx, val = kd.kd_topk_cache_build(h, wt, k)
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1)
+        cache = {"ms": round(cms, 3), "tokens_per_s": n / (cms / 1e3),
+                 "mfma_frac": 2.0 * n * w.vocab * w.d / (cms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)}
+        log(f"cache build {cms:.1f} ms ({cache['tokens_per_s']:.0f} tokens/s)")
+    del wt
+
+    dh_dtype = tdt
+
+    def step():
+        loss, lse, _ = kd.kd_chunked_kl_fwd(h, wd, idx, val, w.tau, chunk_tokens=args.chunk)
+        dh, dw = kd.kd_chunked_kl_bwd(h, wd, idx, val, w.tau, lse, None, dh_dtype=dh_dtype, chunk_tokens=args.chunk)
+        return loss, dh, dw
+
+    for i in range(args.warmup):
+        wl = step()[0].item()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} loss={wl:.5f}")
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    kd.profile_begin()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        out = step()
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    stats = kd.profile_end()
+    peak_gb = torch.cuda.max_memory_allocated(dev) / 1e9
+    loss_val = out[0].item()
+    del out
+    ms = t_total * 1e3 / args.steps
+    value = n / (t_total / args.steps)
+    flops_step = 8.0 * n * w.vocab * w.d
+    peak_tf = BF16_DENSE_PEAK_TFLOPS if w.dtype == "bf16" else FP32_DENSE_PEAK_TFLOPS
+    mfma_util = flops_step / (ms / 1e3) / (peak_tf * 1e12)
+    log(f"{args.steps} steps: {ms:.2f} ms/step, {value:.0f} tokens/s, MFMA {100 * mfma_util:.1f}% of dense peak, "
+        f"peak {peak_gb:.2f} GB, loss={loss_val:.5f}")
+    tot = sum(s["total_ms"] for s in stats.values())
+    for kind, s in sorted(stats.items(), key=lambda kv: -kv[1]["total_ms"]):
+        avg = s["total_ms"] / max(1, s["launches"])
+        tf = s["flops"] / (s["total_ms"] / 1e3) / 1e12 if s["flops"] and s["total_ms"] else 0.0
+        gbs = s["bytes"] / (s["total_ms"] / 1e3) / 1e9 if s["total_ms"] else 0.0
+        log(f"  {kind:14s} {s['launches']:5d} launches  {s['total_ms'] / args.steps:9.3f} ms/step "
+            f"({100 * s['total_ms'] / tot:5.1f}%)  avg {avg:8.3f} ms  {tf:7.1f} TFLOP/s  {gbs:7.1f} GB/s")
+
+    dom_kind, dom = max(stats.items(), key=lambda kv: kv[1]["total_ms"])
+    avg_s = dom["total_ms"] / dom["launches"] / 1e3
+    per_launch_flops = dom["flops"] / dom["launches"]
+    if per_launch_flops > 0:
+        achieved = per_launch_flops / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_tf, 4), "traffic": traffic_for(dom_kind), "kernel": dom_kind,
+                "avg_launch_ms": round(avg_s * 1e3, 4), "flops_per_launch": per_launch_flops}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom_kind), "kernel": dom_kind,
+                "avg_launch_ms": round(avg_s * 1e3, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del h, wd, idx, val
+        torch.cuda.empty_cache()
+        log(f"cpu baseline: float64 oracle on {args.cpu_rows} tokens ...")
+        cpu = cpu_baseline(w, args.cpu_rows, k)
+        log(f"cpu baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "n_tokens": n, "d": w.d, "vocab": w.vocab, "k": k, "tau": w.tau,
+                   "chunk_tokens": args.chunk or "default", "teacher": w.teacher},
+        "mfma_util": round(mfma_util, 4), "peak_gb": round(peak_gb, 3),
+        "roofline": roof, "cpu_baseline": cpu, "cache_build": cache,
+        "kernels_ms_per_step": {k2: round(s["total_ms"] / args.steps, 4) for k2, s in stats.items()},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -154,6 +154,26 @@ kd_status kd_chunked_kl_bwd(const kd_problem* p, const void* h, const void* w,
 /* Static, NUL-terminated description of a status code. */
 const char* kd_status_string(kd_status s);
 
+/* ---- Measurement hooks (not part of the loss; for benchmarks and profiling).
+ * Between kd_profile_begin() and kd_profile_end(), every kernel launch made by the
+ * calls above is bracketed by a pair of HIP events recorded on the call's stream.
+ * kd_profile_end() waits for those events, aggregates them per kernel kind and
+ * disables the hooks. Not thread-safe: one profiling session per process. */
+typedef struct {
+  char name[32];          /* kernel kind, e.g. "gemm_kl_fwd", "gemm_dz", "bucket" */
+  int64_t launches;       /* launches in the session */
+  double total_ms;        /* sum of event-measured durations */
+  double flops;           /* algorithmic FLOPs of all launches (GEMMs: 2*rows*cols*K; else 0) */
+  double bytes;           /* algorithmic HBM bytes of all launches (operands once, outputs once) */
+} kd_kernel_stat;
+
+/* Starts a session (discarding any previous one). */
+kd_status kd_profile_begin(void);
+
+/* Ends the session; writes up to `max` entries to `out` and the number of kernel
+ * kinds seen to *n. Returns KD_ERR_LAUNCH if an event could not be read. */
+kd_status kd_profile_end(kd_kernel_stat* out, int max, int* n);
+
 /* Library ABI version (major * 100 + minor). */
 int kd_version(void);
 

@@ -37,7 +37,7 @@ STATUS_NAMES = {
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd",
-            "kd_status_string", "kd_version")
+            "kd_status_string", "kd_version", "kd_profile_begin", "kd_profile_end")
 
 
 class KDProblem(ctypes.Structure):
@@ -52,6 +52,17 @@ class KDProblem(ctypes.Structure):
         ("val_dtype", ctypes.c_int32),
         ("dh_dtype", ctypes.c_int32),
         ("chunk_tokens", ctypes.c_int32),
+    ]
+
+
+class KDKernelStat(ctypes.Structure):
+    """Mirror of ``kd_kernel_stat``."""
+    _fields_ = [
+        ("name", ctypes.c_char * 32),
+        ("launches", ctypes.c_int64),
+        ("total_ms", ctypes.c_double),
+        ("flops", ctypes.c_double),
+        ("bytes", ctypes.c_double),
     ]
 
 
@@ -85,6 +96,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_status_string.restype = ctypes.c_char_p
     lib.kd_version.argtypes = []
     lib.kd_version.restype = ctypes.c_int
+    lib.kd_profile_begin.argtypes = []
+    lib.kd_profile_begin.restype = ctypes.c_int
+    lib.kd_profile_end.argtypes = [ctypes.POINTER(KDKernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.kd_profile_end.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -212,6 +227,21 @@ def kd_chunked_kl_bwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: 
                                                 _ptr(lse), _ptr(grad), _ptr(dh), _ptr(dw), _ptr(ws), ws.numel(),
                                                 _stream(dev)), "kd_chunked_kl_bwd")
     return dh, dw
+
+
+def profile_begin() -> None:
+    """Start bracketing every kernel launch of the library with HIP events."""
+    _check(load_library().kd_profile_begin(), "kd_profile_begin")
+
+
+def profile_end() -> dict:
+    """Stop the session; returns ``{kind: {launches, total_ms, flops, bytes}}``."""
+    buf = (KDKernelStat * 64)()
+    n = ctypes.c_int(0)
+    _check(load_library().kd_profile_end(buf, 64, ctypes.byref(n)), "kd_profile_end")
+    return {buf[i].name.decode(): {"launches": int(buf[i].launches), "total_ms": float(buf[i].total_ms),
+                                   "flops": float(buf[i].flops), "bytes": float(buf[i].bytes)}
+            for i in range(min(n.value, 64))}
 
 
 class KDChunkedKL(torch.autograd.Function):

@@ -7,7 +7,10 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <string>
 #include <type_traits>
+#include <vector>
+#include <algorithm>
 
 #include "kdkl.h"
 #include "kd_aux.hpp"
@@ -142,6 +145,60 @@ bool debug_checks() {
 
 inline kd_status launched() { return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH; }
 
+// ---- measurement hooks (kd_profile_begin / kd_profile_end)
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+struct Prof {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::string> kinds;
+};
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+hipEvent_t prof_event() {
+  Prof& p = prof();
+  if (!p.pool.empty()) {
+    hipEvent_t e = p.pool.back();
+    p.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+int prof_kind(const char* name) {
+  Prof& p = prof();
+  for (size_t i = 0; i < p.kinds.size(); ++i)
+    if (p.kinds[i] == name) return (int)i;
+  p.kinds.emplace_back(name);
+  return (int)p.kinds.size() - 1;
+}
+
+// Launch `f` (which enqueues one kernel on `st`); bracket it with events when profiling.
+template <typename F>
+kd_status launch(const char* kind, double flops, double bytes, hipStream_t st, F&& f) {
+  Prof& p = prof();
+  hipEvent_t a = nullptr, b = nullptr;
+  if (p.on) {
+    a = prof_event();
+    b = prof_event();
+    if (a && b) hipEventRecord(a, st);
+  }
+  f();
+  const kd_status s = launched();
+  if (p.on && a && b) {
+    hipEventRecord(b, st);
+    p.recs.push_back(ProfRec{prof_kind(kind), a, b, flops, bytes});
+  }
+  return s;
+}
+
 #define KD_TRY(x)                 \
   do {                            \
     const kd_status _s = (x);     \
@@ -165,11 +222,21 @@ GemmArgs gemm_args(const void* X, int64_t ldx, int nx, const void* Y, int64_t ld
 }
 
 template <typename T, int EPI>
-kd_status run_gemm(const GemmArgs& g, hipStream_t st) {
+kd_status run_gemm(const char* kind, const GemmArgs& g, int64_t out_bytes, hipStream_t st) {
   if (g.nx <= 0 || g.ny <= 0) return KD_OK;
   const unsigned blocks = (unsigned)(g.n_tx * g.n_ty);
-  hipLaunchKernelGGL((gemm_kernel<T, EPI>), dim3(blocks), dim3(NTHREADS), 0, st, g);
-  return launched();
+  const double flops = 2.0 * g.nx * (double)g.ny * g.k;
+  const double bytes = (double)sizeof(T) * ((double)g.nx + g.ny) * g.k + (double)out_bytes;
+  return launch(kind, flops, bytes, st, [&] {
+    hipLaunchKernelGGL((gemm_kernel<T, EPI>), dim3(blocks), dim3(NTHREADS), 0, st, g);
+  });
+}
+
+kd_status zero_words(void* p, int64_t n_words, hipStream_t st) {
+  const unsigned blocks = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, cdiv(n_words, 256)));
+  return launch("fill", 0.0, 4.0 * n_words, st, [&] {
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, st, (float*)p, n_words, 0.0f);
+  });
 }
 
 template <typename T>
@@ -182,18 +249,18 @@ kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
   double* bsums = (double*)(ws + L.block_sums);
   int* flags = (int*)(ws + L.flags);
   const bool check = debug_checks();
-  if (check) {
-    if (hipMemsetAsync(flags, 0, sizeof(int) * 4, st) != hipSuccess) return KD_ERR_LAUNCH;
-  }
+  if (check) KD_TRY(zero_words(flags, 4, st));
   const float inv_tau = 1.0f / pl.tau;
+  const int vsz = pl.vdt == KD_BF16 ? 2 : 4;
   for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
     const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
     const int n_tx = (int)cdiv(nr, BX);
     const int32_t* idx_c = idx + r0 * pl.K;
     const size_t hist_bytes = sizeof(int) * (pl.n_ty + 64);
-    hipLaunchKernelGGL(bucket_kernel, dim3(n_tx), dim3(1024), hist_bytes, st, idx_c, nr, pl.K, (int)pl.V, pl.n_ty,
-                       entries, offsets, flags);
-    KD_TRY(launched());
+    KD_TRY(launch("bucket", 0.0, 12.0 * nr * pl.K, st, [&] {
+      hipLaunchKernelGGL(bucket_kernel, dim3(n_tx), dim3(1024), hist_bytes, st, idx_c, nr, pl.K, (int)pl.V,
+                         pl.n_ty, entries, offsets, flags);
+    }));
     GemmArgs g = gemm_args((const T*)h + r0 * pl.d, pl.d, nr, w, pl.d, (int)pl.V, (int)pl.d);
     g.entries = entries;
     g.offsets = offsets;
@@ -201,22 +268,25 @@ kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     g.zg = zg;
     g.partials = partials;
     g.ld_part = pl.Nc;
-    KD_TRY((run_gemm<T, EPI_KL_FWD>(g, st)));
+    KD_TRY((run_gemm<T, EPI_KL_FWD>("gemm_kl_fwd", g, (int64_t)8 * nr * pl.n_ty, st)));
     const int nb = (int)cdiv(nr, 256);
-    if (pl.vdt == KD_BF16)
-      hipLaunchKernelGGL(merge_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty, idx_c,
-                         (const bf16_t*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
-                         kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / 256);
-    else
-      hipLaunchKernelGGL(merge_kernel<float>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty, idx_c,
-                         (const float*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
-                         kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / 256);
-    KD_TRY(launched());
+    const double mbytes = (double)nr * (8.0 * pl.n_ty + pl.K * (8.0 + vsz) + 8.0);
+    KD_TRY(launch("merge", 0.0, mbytes, st, [&] {
+      if (pl.vdt == KD_BF16)
+        hipLaunchKernelGGL(merge_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty,
+                           idx_c, (const bf16_t*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
+                           kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / 256);
+      else
+        hipLaunchKernelGGL(merge_kernel<float>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty,
+                           idx_c, (const float*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
+                           kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / 256);
+    }));
   }
   const int nb_all = (int)cdiv(pl.N, 256);
-  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsums, nb_all,
-                     pl.N > 0 ? 1.0 / (double)pl.N : 0.0, loss);
-  KD_TRY(launched());
+  KD_TRY(launch("loss", 0.0, 8.0 * nb_all, st, [&] {
+    hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsums, nb_all, pl.N > 0 ? 1.0 / (double)pl.N : 0.0,
+                       loss);
+  }));
   if (check) {
     int bad = 0;
     if (hipMemcpyAsync(&bad, flags, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return KD_ERR_LAUNCH;
@@ -230,28 +300,28 @@ template <typename T>
 kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
                    const void* val, const float* lse, const float* grad, void* dh, float* dw, char* ws,
                    hipStream_t st) {
-  if (pl.N == 0) {
-    hipLaunchKernelGGL(fill_f32_kernel, dim3(1024), dim3(256), 0, st, dw, pl.V * pl.d, 0.0f);
-    return launched();
-  }
+  if (pl.N == 0) return zero_words(dw, pl.V * pl.d, st);
   T* wt = (T*)(ws + L.wt);
   T* ht = (T*)(ws + L.ht);
   T* dz = (T*)(ws + L.dz);
   T* dzt = (T*)(ws + L.dzt);
   const float inv_n = 1.0f / (float)pl.N;
   const float inv_tau = 1.0f / pl.tau;
+  const int64_t es = (int64_t)sizeof(T);
   // W^T [d][V_pad], zero past V
-  hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(pl.V_pad, 64), (unsigned)cdiv(pl.d, 64)),
-                     dim3(256), 0, st, (const T*)w, pl.d, (int)pl.V, (int)pl.d, wt, pl.V_pad, (int)pl.V_pad);
-  KD_TRY(launched());
+  KD_TRY(launch("transpose_w", 0.0, 2.0 * es * pl.V * pl.d, st, [&] {
+    hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(pl.V_pad, 64), (unsigned)cdiv(pl.d, 64)),
+                       dim3(256), 0, st, (const T*)w, pl.d, (int)pl.V, (int)pl.d, wt, pl.V_pad, (int)pl.V_pad);
+  }));
   for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
     const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
     const int nr64 = (int)round_up(nr, 64);
     const T* hc = (const T*)h + r0 * pl.d;
     // H^T [d][Nc], zero past nr
-    hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(nr64, 64), (unsigned)cdiv(pl.d, 64)), dim3(256),
-                       0, st, hc, pl.d, nr, (int)pl.d, ht, pl.Nc, nr64);
-    KD_TRY(launched());
+    KD_TRY(launch("transpose_h", 0.0, 2.0 * es * nr * pl.d, st, [&] {
+      hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(nr64, 64), (unsigned)cdiv(pl.d, 64)),
+                         dim3(256), 0, st, hc, pl.d, nr, (int)pl.d, ht, pl.Nc, nr64);
+    }));
     // recompute logits, dZ = (g/N) softmax
     GemmArgs g = gemm_args(hc, pl.d, nr, w, pl.d, (int)pl.V, (int)pl.d);
     g.out = dz;
@@ -263,18 +333,19 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     g.lse = lse + r0;
     g.grad = grad;
     g.inv_n = inv_n;
-    KD_TRY((run_gemm<T, EPI_KL_DZ>(g, st)));
+    KD_TRY((run_gemm<T, EPI_KL_DZ>("gemm_dz", g, 2 * es * nr * pl.V, st)));
     // subtract the teacher at the cached entries
     const int nb = (int)cdiv(nr, 256);
-    if (pl.vdt == KD_BF16)
-      hipLaunchKernelGGL((scatter_kernel<T, bf16_t>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
-                         (const bf16_t*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.V_pad, dzt,
-                         pl.Nc);
-    else
-      hipLaunchKernelGGL((scatter_kernel<T, float>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
-                         (const float*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.V_pad, dzt,
-                         pl.Nc);
-    KD_TRY(launched());
+    KD_TRY(launch("scatter", 0.0, (double)nr * pl.K * (8.0 + 4.0 * es), st, [&] {
+      if (pl.vdt == KD_BF16)
+        hipLaunchKernelGGL((scatter_kernel<T, bf16_t>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
+                           (const bf16_t*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.V_pad,
+                           dzt, pl.Nc);
+      else
+        hipLaunchKernelGGL((scatter_kernel<T, float>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
+                           (const float*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.V_pad,
+                           dzt, pl.Nc);
+    }));
     // dH = dZ W  (P[t][j] = sum_v dZ[t][v] W^T[j][v])
     GemmArgs gh = gemm_args(dz, pl.V_pad, nr, wt, pl.V_pad, (int)pl.d, (int)pl.V_pad);
     gh.out_rows = nr;
@@ -282,10 +353,10 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     gh.ldo = pl.d;
     if (pl.dhdt == KD_F32) {
       gh.out = (float*)dh + r0 * pl.d;
-      KD_TRY((run_gemm<T, EPI_STORE_F32>(gh, st)));
+      KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_dh", gh, 4 * nr * pl.d, st)));
     } else {
       gh.out = (bf16_t*)dh + r0 * pl.d;
-      KD_TRY((run_gemm<T, EPI_STORE_BF16>(gh, st)));
+      KD_TRY((run_gemm<T, EPI_STORE_BF16>("gemm_dh", gh, 2 * nr * pl.d, st)));
     }
     // dW (+)= dZ^T H  (P[v][j] = sum_t dZ^T[v][t] H^T[j][t])
     GemmArgs gw = gemm_args(dzt, pl.Nc, (int)pl.V, ht, pl.Nc, (int)pl.d, nr64);
@@ -294,7 +365,7 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     gw.out_rows = (int)pl.V;
     gw.out_cols = (int)pl.d;
     gw.accumulate = r0 > 0;
-    KD_TRY((run_gemm<T, EPI_STORE_F32>(gw, st)));
+    KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_dw", gw, (r0 > 0 ? 8 : 4) * pl.V * pl.d, st)));
   }
   return KD_OK;
 }
@@ -308,12 +379,16 @@ kd_status topk_impl(const Plan& pl, const Layout& L, const void* ht, const void*
   double* wmax = (double*)(ws + L.wmax);
   int* overflow = (int*)(ws + L.overflow);
   const bool check = debug_checks();
-  if (check && hipMemsetAsync(overflow, 0, sizeof(int) * 4, st) != hipSuccess) return KD_ERR_LAUNCH;
+  if (check) KD_TRY(zero_words(overflow, 4, st));
+  const int64_t es = (int64_t)sizeof(T);
   const int nblk = (int)std::min<int64_t>(1024, cdiv(pl.V, 4));
-  hipLaunchKernelGGL(rownorm_max_kernel<T>, dim3(nblk), dim3(256), 0, st, (const T*)wt, (int)pl.V, (int)pl.d, bmax);
-  KD_TRY(launched());
-  hipLaunchKernelGGL(max_reduce_kernel, dim3(1), dim3(256), 0, st, bmax, nblk, wmax);
-  KD_TRY(launched());
+  KD_TRY(launch("rownorm", 0.0, (double)es * pl.V * pl.d, st, [&] {
+    hipLaunchKernelGGL(rownorm_max_kernel<T>, dim3(nblk), dim3(256), 0, st, (const T*)wt, (int)pl.V, (int)pl.d,
+                       bmax);
+  }));
+  KD_TRY(launch("rownorm", 0.0, 8.0 * nblk, st, [&] {
+    hipLaunchKernelGGL(max_reduce_kernel, dim3(1), dim3(256), 0, st, bmax, nblk, wmax);
+  }));
   for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
     const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
     const T* hc = (const T*)ht + r0 * pl.d;
@@ -322,10 +397,11 @@ kd_status topk_impl(const Plan& pl, const Layout& L, const void* ht, const void*
     g.ldo = pl.V_pad;
     g.out_rows = nr;
     g.out_cols = (int)pl.V_pad;
-    KD_TRY((run_gemm<T, EPI_STORE_F32>(g, st)));
-    hipLaunchKernelGGL((topk_select_kernel<T, VT>), dim3(nr), dim3(SEL_THREADS), 0, st, S, pl.V_pad, (int)pl.V,
-                       pl.K, hc, (int)pl.d, (const T*)wt, wmax, idx + r0 * pl.K, (VT*)val + r0 * pl.K, overflow);
-    KD_TRY(launched());
+    KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_topk", g, 4 * nr * pl.V_pad, st)));
+    KD_TRY(launch("topk_select", 0.0, 12.0 * nr * pl.V_pad + (double)nr * pl.K * (4 + sizeof(VT)), st, [&] {
+      hipLaunchKernelGGL((topk_select_kernel<T, VT>), dim3(nr), dim3(SEL_THREADS), 0, st, S, pl.V_pad, (int)pl.V,
+                         pl.K, hc, (int)pl.d, (const T*)wt, wmax, idx + r0 * pl.K, (VT*)val + r0 * pl.K, overflow);
+    }));
   }
   if (check) {
     int ov = 0;
@@ -423,5 +499,43 @@ const char* kd_status_string(kd_status s) {
 }
 
 int kd_version(void) { return 100; }
+
+kd_status kd_profile_begin(void) {
+  Prof& p = prof();
+  for (auto& r : p.recs) {
+    p.pool.push_back(r.a);
+    p.pool.push_back(r.b);
+  }
+  p.recs.clear();
+  p.kinds.clear();
+  p.on = true;
+  return KD_OK;
+}
+
+kd_status kd_profile_end(kd_kernel_stat* out, int max, int* n) {
+  Prof& p = prof();
+  p.on = false;
+  kd_status st = KD_OK;
+  std::vector<kd_kernel_stat> agg(p.kinds.size());
+  for (size_t i = 0; i < p.kinds.size(); ++i) {
+    std::memset(&agg[i], 0, sizeof(kd_kernel_stat));
+    std::strncpy(agg[i].name, p.kinds[i].c_str(), sizeof(agg[i].name) - 1);
+  }
+  for (auto& r : p.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) st = KD_ERR_LAUNCH;
+    kd_kernel_stat& a = agg[(size_t)r.kind];
+    a.launches += 1;
+    a.total_ms += ms;
+    a.flops += r.flops;
+    a.bytes += r.bytes;
+    p.pool.push_back(r.a);
+    p.pool.push_back(r.b);
+  }
+  p.recs.clear();
+  if (n) *n = (int)agg.size();
+  for (int i = 0; out && i < max && i < (int)agg.size(); ++i) out[i] = agg[(size_t)i];
+  return st;
+}
 
 }  // extern "C"

@@ -89,9 +89,11 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=0, help="override N (e.g. a sweep point)")
     ap.add_argument("--k", type=int, default=0, help="override K")
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = library default)")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-build-timing", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -106,6 +108,16 @@ def main() -> int:
 
     import kd_synth
     import lm_head_kl_amd as kd
+
+    if args.calibrate_copy_mib:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.calibrate_copy_mib} MiB twice (read {nbytes} B, write {nbytes} B per copy)")
+        return 0
 
     kd.load_library()
     dev = torch.device("cuda:0")

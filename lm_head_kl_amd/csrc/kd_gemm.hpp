@@ -8,41 +8,67 @@
 //   dW[v][j]          : X = dZ^T rows (vocab),   Y = H^T rows (hidden),   K = tokens
 //   teacher S[t][v]   : X = H_T rows,            Y = W_T rows,            K = d
 //
-// Workgroup tile 256 (n) x 256 (m), 8 waves arranged 4 (n) x 2 (m), each wave
-// owning 64 x 128 outputs as 4 x 8 MFMA 16x16 blocks (128 fp32 accumulators per
-// lane).  K is staged 128 bytes per row per stage (64 bf16 / 32 fp32) through a
-// double-buffered, row-padded LDS tile: the global loads of stage s+1 are in
-// flight while stage s feeds the MFMAs.  bf16 uses v_mfma_f32_16x16x32_bf16; fp32
-// uses four v_mfma_f32_16x16x4_f32 over the same 16-byte fragment.
+// Main loop (one workgroup per BX x BY output tile, 8 waves of 64 x 128 outputs):
+//  * operands reach LDS through wave-wide buffer loads that write LDS directly
+//    (no staging registers, no ds_write); rows past an operand's end and K past
+//    its end read as zero (out-of-range buffer offsets), so tails need no branches;
+//  * LDS holds NS = 5 stages of 64 bytes of K per row; the load of stage kt + 4 is
+//    issued while stage kt is multiplied, so a load has three stages of MFMA work
+//    to land; one barrier per stage;
+//  * the 16-byte chunks of each LDS row are XOR-swizzled by (row / 2) % 4, which
+//    makes the MFMA fragment reads (ds_read_b128, lane = row l % 16, chunk l / 16)
+//    free of bank conflicts on gfx950 (measured: 4 LDS cycles per read);
+//  * the fragments of stage kt + 1 are read from LDS during the MFMAs of stage kt;
+//  * bf16 uses v_mfma_f32_16x16x32_bf16; fp32 uses four v_mfma_f32_16x16x4_f32 on
+//    the same 16-byte fragment.
 //
-// MFMA 16x16 lane layout used throughout: operand lane l supplies row (l % 16)
-// and a 16-byte K slice (l / 16); the result lane l holds column n = l % 16 and
-// rows m = 4 * (l / 16) + e, e = 0..3.  Here the Y fragment is the MFMA "A"
-// operand (m) and the X fragment the "B" operand (n).
+// MFMA 16x16 lane layout: operand lane l supplies row (l % 16) and the 16-byte K
+// slice (l / 16); result lane l holds column n = l % 16 and rows m = 4(l/16)+e.
+// The Y fragment is the MFMA "A" operand (m), the X fragment the "B" operand (n).
 #pragma once
+
+#include <type_traits>
 
 #include "kd_common.hpp"
 
 namespace kd {
 
-constexpr int BX = 256, BY = 256;
-constexpr int KBYTES = 128;                 // K bytes per row per stage
-constexpr int PITCH = KBYTES + 16;          // padded LDS row pitch (bytes)
-constexpr int WAVES_X = 4, WAVES_Y = 2;
-constexpr int NWAVES = WAVES_X * WAVES_Y;
-constexpr int NTHREADS = 64 * NWAVES;       // 512
-constexpr int WX = BX / WAVES_X;            // 64
-constexpr int WY = BY / WAVES_Y;            // 128
-constexpr int FX = WX / 16, FY = WY / 16;   // 4 x 8 MFMA blocks per wave
-constexpr int STAGE_BYTES = (BX + BY) * PITCH;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;  // 147456 of the 160 KiB per CU
+template <int BX_, int BY_, int WAVES_X_, int WAVES_Y_, int KB_, int NS_>
+struct GemmCfg {
+  static constexpr int BX = BX_, BY = BY_;
+  static constexpr int WAVES_X = WAVES_X_, WAVES_Y = WAVES_Y_;
+  static constexpr int NWAVES = WAVES_X * WAVES_Y;
+  static constexpr int NTHREADS = 64 * NWAVES;
+  static constexpr int WX = BX / WAVES_X, WY = BY / WAVES_Y;
+  static constexpr int FX = WX / 16, FY = WY / 16;
+  static constexpr int KB = KB_;                        // K bytes per row per stage
+  static constexpr int CPR = KB / 16;                   // 16-byte chunks per row
+  static constexpr int STAGE_BYTES = (BX + BY) * KB;
+  static constexpr int NS = NS_;                        // LDS stages
+  static constexpr int MAIN_LDS = NS * STAGE_BYTES;
+  static constexpr int DMA_PER_WAVE = STAGE_BYTES / 1024 / NWAVES;   // 1 KB wave-wide loads per stage
+  static_assert(NS >= 4 && STAGE_BYTES % (1024 * NWAVES) == 0 && (BX * KB) % 1024 == 0, "DMA blocks");
+  static_assert((BX * KB / 1024) % DMA_PER_WAVE == 0, "a wave's blocks are all X or all Y");
+  static_assert(KB == 64, "one 16x16x32 fragment (64 bytes of K) per row per stage");
+  static_assert(WX % 16 == 0 && WY % 64 == 0, "wave tile");
+  // chunk swizzle of LDS row r (conflict-free ds_read_b128 fragment reads)
+  __device__ __forceinline__ static int swz(int r) { return (r >> 1) & 3; }
+};
 
-// Epilogue staging of the forward gather: per wave 64 tokens x 64 vocabulary
-// floats (two rounds cover the wave's 128 vocabulary columns).
-constexpr int SPITCH = 68;                                      // floats
-constexpr int STAGE_WAVE_FLOATS = WX * SPITCH;
-constexpr int STATS_OFF = NWAVES * STAGE_WAVE_FLOATS * 4;       // bytes
-static_assert(STATS_OFF + WAVES_Y * BX * 8 <= LDS_BYTES, "epilogue LDS");
+// The library's configuration: 256 x 256 tiles, 8 waves (4 along X, 2 along Y),
+// 64 x 128 outputs per wave, 64-byte K stages, 5 LDS stages (160 KiB).
+typedef GemmCfg<256, 256, 4, 2, 64, 5> MainCfg;
+
+constexpr int BX = MainCfg::BX, BY = MainCfg::BY;
+
+// Epilogue staging of the forward gather: per wave WX tokens x 64 vocabulary floats.
+constexpr int SPITCH = 68;   // floats per staged token row
+template <class C> constexpr int stage_wave_floats() { return C::WX * SPITCH; }
+template <class C> constexpr int stats_off() { return C::NWAVES * stage_wave_floats<C>() * 4; }
+template <class C> constexpr int fwd_lds() { return stats_off<C>() + C::WAVES_Y * C::BX * 8; }
+template <class C, int EPI> constexpr int kernel_lds() {
+  return (EPI == 2 && fwd_lds<C>() > C::MAIN_LDS) ? fwd_lds<C>() : C::MAIN_LDS;
+}
 
 enum Epi : int {
   EPI_STORE_F32 = 0,   // P -> float out (optionally += existing)
@@ -75,7 +101,7 @@ struct GemmArgs {
 
 // Workgroup -> tile.  Each XCD receives one contiguous range of the logical
 // order, and the logical order walks `group` X-tiles for every Y-tile, so the
-// 32 tiles that one XCD runs at a time share X and Y strips in its L2.
+// tiles that one XCD runs at a time share X and Y strips in its L2.
 __device__ __forceinline__ void tile_of(int bid, int n_tx, int n_ty, int group, int& tx, int& ty) {
   const int n = n_tx * n_ty;
   const int per = n / kXcds, rem = n % kXcds;
@@ -120,53 +146,50 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename T, int EPI>
-__global__ void __launch_bounds__(NTHREADS, 1) gemm_kernel(const GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-  constexpr int EPC = 16 / int(sizeof(T));      // elements per 16-byte chunk
-  constexpr int KE = KBYTES / int(sizeof(T));   // elements per stage
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any operand: loads return 0
+
+// One wave-wide 16-byte-per-lane buffer load written straight into LDS: lane i's
+// data lands at LDS byte address lds_addr + 16 i (lds_addr wave-uniform).  It has no
+// destination register; completion is tracked with s_waitcnt vmcnt by the caller.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const u32x4& rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Raw buffer descriptor (gfx9 layout) in scalar registers.
+__device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+template <class C, typename T, int EPI>
+__global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kernel_lds<C, EPI>()];
+  constexpr int ES = int(sizeof(T));
+  constexpr int EPC = 16 / ES;            // elements per 16-byte chunk
+  constexpr int KE = C::KB / ES;          // elements per stage
+  constexpr int FX = C::FX, FY = C::FY, WX = C::WX, WY = C::WY, BXc = C::BX, BYc = C::BY;
 
   int tx, ty;
   tile_of(blockIdx.x, a.n_tx, a.n_ty, a.group, tx, ty);
-  const int x0 = tx * BX, y0 = ty * BY;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wx = wave % WAVES_X, wy = wave / WAVES_X;
+  const int x0 = tx * BXc, y0 = ty * BYc;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wx = wave % C::WAVES_X, wy = wave / C::WAVES_X;
 
-  // ---- loader: thread owns 16-byte chunk (row lrow + 64 j, column lq) of X and Y
-  const T* Xb = (const T*)a.X + (int64_t)x0 * a.ldx;
-  const T* Yb = (const T*)a.Y + (int64_t)y0 * a.ldy;
-  const int xrows = min(BX, a.nx - x0), yrows = min(BY, a.ny - y0);
-  const int lrow = tid >> 3, lq = tid & 7;
-  const int kq = lq * EPC;
-  uint32_t xoff[4], yoff[4];
-  bool xok[4], yok[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = lrow + 64 * j;
-    xok[j] = r < xrows;
-    yok[j] = r < yrows;
-    xoff[j] = uint32_t((xok[j] ? r : 0) * a.ldx + kq);
-    yoff[j] = uint32_t((yok[j] ? r : 0) * a.ldy + kq);
-  }
-  const uint32_t lds_st = uint32_t(lrow * PITCH + lq * 16);
-
-  u32x4 stg[8];
-  auto gload = [&](int k0) {
-    const bool kok = (k0 + kq) < a.k;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      stg[j] = (kok && xok[j]) ? *(const u32x4*)(Xb + xoff[j] + k0) : u32x4{0u, 0u, 0u, 0u};
-      stg[4 + j] = (kok && yok[j]) ? *(const u32x4*)(Yb + yoff[j] + k0) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto lstore = [&](int s) {
-    char* base = lds + s * STAGE_BYTES + lds_st;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *(u32x4*)(base + 64 * j * PITCH) = stg[j];
-      *(u32x4*)(base + (BX + 64 * j) * PITCH) = stg[4 + j];
-    }
-  };
+  const int xrows = min(BXc, a.nx - x0), yrows = min(BYc, a.ny - y0);
 
   f32x4 acc[FX][FY];
 #pragma unroll
@@ -174,37 +197,79 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < FY; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t xs_off = uint32_t((wx * WX + (lane & 15)) * PITCH + (lane >> 4) * 16);
-  const uint32_t ys_off = uint32_t((BX + wy * WY + (lane & 15)) * PITCH + (lane >> 4) * 16);
-  auto compute = [&](int s) {
-    const char* base = lds + s * STAGE_BYTES;
+  // per-lane fragment read offsets (fragment rows start at multiples of 16, so the
+  // swizzle depends only on lane % 16)
+  const int fr = lane & 15, fq = lane >> 4;
+  const uint32_t xs = uint32_t((wx * WX + fr) * C::KB + ((fq ^ C::swz(fr)) * 16));
+  const uint32_t ys = uint32_t((BXc + wy * WY + fr) * C::KB + ((fq ^ C::swz(fr)) * 16));
+  const int nk = (a.k + KE - 1) / KE;
+  {
+    // ---- LDS-DMA pipeline: stage s lives in LDS buffer s % NS; the DMA for stage
+    // kt + NS - 1 is issued in iteration kt, and the fragments of stage kt + 1 are
+    // read from LDS while the MFMAs of stage kt run.
+    constexpr int DPW = C::DMA_PER_WAVE;
+    constexpr int RPB = 1024 / C::KB;                    // rows per 1 KB DMA block
+    constexpr int XBLK = BXc * C::KB / 1024;             // X blocks per stage
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    const u32x4 xd = buffer_desc((const T*)a.X + (int64_t)x0 * a.ldx, (uint32_t)(xrows * a.ldx * ES));
+    const u32x4 yd = buffer_desc((const T*)a.Y + (int64_t)y0 * a.ldy, (uint32_t)(yrows * a.ldy * ES));
+    // block b of a stage: rows b*RPB .. of X (b < XBLK) or of Y; lane -> (row, swizzled chunk)
+    uint32_t voff[DPW];
+    int vch[DPW];
+    const int brow = lane / C::CPR, bp = lane % C::CPR;
 #pragma unroll
-    for (int f = 0; f < KBYTES / 64; ++f) {
-      u32x4 bx[FX], by[FY];
+    for (int q = 0; q < DPW; ++q) {
+      const int b = wave * DPW + q;
+      const bool isx = b < XBLK;
+      const int row = (isx ? b : b - XBLK) * RPB + brow;
+      const int ch = bp ^ C::swz(row);
+      vch[q] = ch * EPC;
+      voff[q] = uint32_t(row * (isx ? a.ldx : a.ldy) * ES + ch * 16);
+    }
+    const bool wave_x = wave * DPW < XBLK;               // a wave's blocks are all X or all Y
+    auto issue = [&](int stage) {
+      const int k0 = stage * KE;
+      const int buf = stage % C::NS;
 #pragma unroll
-      for (int i = 0; i < FX; ++i) bx[i] = *(const u32x4*)(base + xs_off + i * 16 * PITCH + f * 64);
+      for (int q = 0; q < DPW; ++q) {
+        const uint32_t o = (k0 + vch[q] < a.k) ? voff[q] + uint32_t(k0 * ES) : kOOB;
+        dma16(lds_base + uint32_t(buf * C::STAGE_BYTES + (wave * DPW + q) * 1024), o, wave_x ? xd : yd);
+      }
+    };
+    auto rdfrag = [&](u32x4 (&bx)[FX], u32x4 (&by)[FY], int stage) {
+      const char* base = lds + (stage % C::NS) * C::STAGE_BYTES;
 #pragma unroll
-      for (int j = 0; j < FY; ++j) by[j] = *(const u32x4*)(base + ys_off + j * 16 * PITCH + f * 64);
+      for (int i = 0; i < FX; ++i) bx[i] = *(const u32x4*)(base + xs + i * 16 * C::KB);
+#pragma unroll
+      for (int j = 0; j < FY; ++j) by[j] = *(const u32x4*)(base + ys + j * 16 * C::KB);
+    };
+#pragma unroll
+    for (int s = 0; s < C::NS - 1; ++s) issue(s);
+    wait_vmcnt<DPW * (C::NS - 2)>();
+    __syncthreads();
+    u32x4 fa_x[FX], fa_y[FY], fb_x[FX], fb_y[FY];
+    auto step = [&](int kt, u32x4 (&cx)[FX], u32x4 (&cy)[FY], u32x4 (&nx_)[FX], u32x4 (&ny_)[FY]) {
+      wait_vmcnt<DPW * (C::NS - 3)>();                 // own loads of stage kt + 1 have landed
+      __syncthreads();                                   // everyone's; and buffer (kt-1) % NS is free
+      issue(kt + C::NS - 1);
+      rdfrag(nx_, ny_, kt + 1);
 #pragma unroll
       for (int i = 0; i < FX; ++i)
 #pragma unroll
-        for (int j = 0; j < FY; ++j) Mma<T>::run(acc[i][j], by[j], bx[i]);
+        for (int j = 0; j < FY; ++j) Mma<T>::run(acc[i][j], cy[j], cx[i]);
+    };
+    rdfrag(fa_x, fa_y, 0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, fa_x, fa_y, fb_x, fb_y);
+      step(kt + 1, fb_x, fb_y, fa_x, fa_y);
     }
-  };
-
-  const int nk = (a.k + KE - 1) / KE;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) gload((kt + 1) * KE);
-    compute(kt & 1);
-    if (more) lstore((kt + 1) & 1);
+    if (kt < nk) step(kt, fa_x, fa_y, fb_x, fb_y);
+    wait_vmcnt<0>();
     __syncthreads();
   }
 
-  // ---- epilogues.  Lane (i, j, e) holds P[n = x0 + wx*64 + i*16 + lane%16][m = mcol + j*16 + e].
+  // ---- epilogues.  Lane (i, j, e) holds P[n = x0 + wx*WX + i*16 + lane%16][m = mcol + j*16 + e].
   const int nrow0 = x0 + wx * WX + (lane & 15);
   const int mcol = y0 + wy * WY + (lane >> 4) * 4;
 
@@ -227,7 +292,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_kernel(const GemmArgs a) {
       }
     }
   } else if constexpr (EPI == EPI_KL_FWD) {
-    // (1) per-token max and sum of exp over this wave's 128 vocabulary columns.
+    // (1) per-token max and sum of exp over this wave's WY vocabulary columns.
     float tm[FX], ts[FX];
 #pragma unroll
     for (int i = 0; i < FX; ++i) {
@@ -253,19 +318,19 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_kernel(const GemmArgs a) {
       tm[i] = mx;
       ts[i] = s;
     }
-    // (2) merge the two waves that share these tokens; one partial per (row, vocab tile).
-    float2* st = (float2*)(lds + STATS_OFF);
+    // (2) merge the waves that share these tokens; one partial per (row, vocab tile).
+    float2* st = (float2*)(lds + stats_off<C>());
     if ((lane >> 4) == 0) {
 #pragma unroll
-      for (int i = 0; i < FX; ++i) st[wy * BX + wx * WX + i * 16 + lane] = make_float2(tm[i], ts[i]);
+      for (int i = 0; i < FX; ++i) st[wy * BXc + wx * WX + i * 16 + lane] = make_float2(tm[i], ts[i]);
     }
     // (3) gather the cached entries that fall in this tile (wave-private LDS staging).
-    float* sw = (float*)lds + wave * STAGE_WAVE_FLOATS;
+    float* sw = (float*)lds + wave * stage_wave_floats<C>();
     const int* off = a.offsets + (int64_t)tx * (a.n_ty + 1) + ty;
     const int eb = off[0], ee = off[1];
-    const uint32_t* ent = a.entries + (int64_t)tx * BX * a.kc;
+    const uint32_t* ent = a.entries + (int64_t)tx * BXc * a.kc;
 #pragma unroll
-    for (int rnd = 0; rnd < 2; ++rnd) {
+    for (int rnd = 0; rnd < WY / 64; ++rnd) {
 #pragma unroll
       for (int i = 0; i < FX; ++i)
 #pragma unroll
@@ -282,11 +347,18 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_kernel(const GemmArgs a) {
       wave_sync_lds();
     }
     __syncthreads();
-    if (tid < BX) {
-      const float2 p0 = st[tid], p1 = st[BX + tid];
-      const float M = fmaxf(p0.x, p1.x);
+    if (tid < BXc) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < C::WAVES_Y; ++w) M = fmaxf(M, st[w * BXc + tid].x);
       float S = 0.f;
-      if (M != -INFINITY) S = p0.y * fast_exp2((p0.x - M) * kLog2e) + p1.y * fast_exp2((p1.x - M) * kLog2e);
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < C::WAVES_Y; ++w) {
+          const float2 p = st[w * BXc + tid];
+          S += p.y * fast_exp2((p.x - M) * kLog2e);
+        }
+      }
       const int row = x0 + tid;
       if (row < a.nx) a.partials[(int64_t)ty * a.ld_part + row] = make_float2(M, S);
     }

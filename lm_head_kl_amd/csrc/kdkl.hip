@@ -25,10 +25,18 @@ constexpr int kMaxK = 65535;             // k fits the 16-bit field of a bucket 
 constexpr int kMaxKTopk = 4096;          // selection candidates are held in LDS
 constexpr int64_t kDefaultChunkKL = 16384;
 constexpr int64_t kDefaultChunkTopk = 8192;
-constexpr int kGroup = 8;
+constexpr int kGroup = 4;   // X tiles walked per Y tile (measured best for all four GEMM shapes)
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// Leading dimension of an internal buffer: a multiple of 64 elements whose byte
+// stride is not a multiple of 4 KiB (power-of-two strides put all rows of a tile
+// on the same L2 channels; measured 25% slower on the dW GEMM).
+inline int64_t pad_ld(int64_t n, int64_t esz) {
+  int64_t l = round_up(n, 64);
+  if ((l * esz) % 4096 == 0) l += 64;
+  return l;
+}
 
 struct Plan {
   int64_t N, d, V;
@@ -38,6 +46,8 @@ struct Plan {
   int64_t esz;      // bytes per H/W element
   int64_t Nc;       // tokens per chunk (multiple of 256)
   int64_t V_pad;    // vocabulary rounded up to 64 (K-extent of dH)
+  int64_t ld_v;     // leading dimension of dZ, W^T and the teacher logits (>= V_pad)
+  int64_t ld_t;     // leading dimension of dZ^T and H^T (>= Nc)
   int n_ty;         // 256-wide vocabulary tiles
 };
 
@@ -82,10 +92,13 @@ kd_status validate(kd_op op, const kd_problem* p, Plan* pl) {
   c = std::min<int64_t>(c, round_up(std::max<int64_t>(pl->N, 1), BX));
   pl->Nc = c;
   pl->V_pad = round_up(pl->V, 64);
+  pl->ld_v = pad_ld(pl->V_pad, op == KD_OP_TOPK_BUILD ? 4 : pl->esz);
+  pl->ld_t = pad_ld(pl->Nc, pl->esz);
   pl->n_ty = (int)cdiv(pl->V, BY);
   // 32-bit offsets inside one 256-row tile of every GEMM operand
-  if (!mul_ok(BX, std::max<int64_t>(pl->V_pad, pl->d) + 64, INT32_MAX)) return KD_ERR_BAD_SHAPE;
-  if (!mul_ok(pl->Nc, pl->V_pad) || !mul_ok(pl->d, pl->V_pad)) return KD_ERR_BAD_SHAPE;
+  // 32-bit byte offsets inside one 256-row tile of every GEMM operand
+  if (!mul_ok(BX * 4, std::max<int64_t>(std::max<int64_t>(pl->ld_v, pl->ld_t), pl->d), INT32_MAX))
+    return KD_ERR_BAD_SHAPE;
   return KD_OK;
 }
 
@@ -106,12 +119,12 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     L->block_sums = take(sizeof(double) * (size_t)std::max<int64_t>(1, cdiv(pl.N, 256)));
     L->flags = take(sizeof(int) * 4);
   } else if (op == KD_OP_KL_BWD) {
-    L->wt = take((size_t)(pl.esz * pl.d * pl.V_pad));
-    L->ht = take((size_t)(pl.esz * pl.d * pl.Nc));
-    L->dz = take((size_t)(pl.esz * pl.Nc * pl.V_pad));
-    L->dzt = take((size_t)(pl.esz * pl.V_pad * pl.Nc));
+    L->wt = take((size_t)(pl.esz * pl.d * pl.ld_v));
+    L->ht = take((size_t)(pl.esz * pl.d * pl.ld_t));
+    L->dz = take((size_t)(pl.esz * pl.Nc * pl.ld_v));
+    L->dzt = take((size_t)(pl.esz * pl.V_pad * pl.ld_t));
   } else {
-    L->s = take(sizeof(float) * (size_t)(pl.Nc * pl.V_pad));
+    L->s = take(sizeof(float) * (size_t)(pl.Nc * pl.ld_v));
     L->bmax = take(sizeof(double) * 1024);
     L->wmax = take(sizeof(double));
     L->overflow = take(sizeof(int) * 4);
@@ -228,7 +241,7 @@ kd_status run_gemm(const char* kind, const GemmArgs& g, int64_t out_bytes, hipSt
   const double flops = 2.0 * g.nx * (double)g.ny * g.k;
   const double bytes = (double)sizeof(T) * ((double)g.nx + g.ny) * g.k + (double)out_bytes;
   return launch(kind, flops, bytes, st, [&] {
-    hipLaunchKernelGGL((gemm_kernel<T, EPI>), dim3(blocks), dim3(NTHREADS), 0, st, g);
+    hipLaunchKernelGGL((gemm_kernel<MainCfg, T, EPI>), dim3(blocks), dim3(MainCfg::NTHREADS), 0, st, g);
   });
 }
 
@@ -311,7 +324,7 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
   // W^T [d][V_pad], zero past V
   KD_TRY(launch("transpose_w", 0.0, 2.0 * es * pl.V * pl.d, st, [&] {
     hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(pl.V_pad, 64), (unsigned)cdiv(pl.d, 64)),
-                       dim3(256), 0, st, (const T*)w, pl.d, (int)pl.V, (int)pl.d, wt, pl.V_pad, (int)pl.V_pad);
+                       dim3(256), 0, st, (const T*)w, pl.d, (int)pl.V, (int)pl.d, wt, pl.ld_v, (int)pl.V_pad);
   }));
   for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
     const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
@@ -320,14 +333,14 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     // H^T [d][Nc], zero past nr
     KD_TRY(launch("transpose_h", 0.0, 2.0 * es * nr * pl.d, st, [&] {
       hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(nr64, 64), (unsigned)cdiv(pl.d, 64)),
-                         dim3(256), 0, st, hc, pl.d, nr, (int)pl.d, ht, pl.Nc, nr64);
+                         dim3(256), 0, st, hc, pl.d, nr, (int)pl.d, ht, pl.ld_t, nr64);
     }));
     // recompute logits, dZ = (g/N) softmax
     GemmArgs g = gemm_args(hc, pl.d, nr, w, pl.d, (int)pl.V, (int)pl.d);
     g.out = dz;
-    g.ldo = pl.V_pad;
+    g.ldo = pl.ld_v;
     g.out2 = dzt;
-    g.ldo2 = pl.Nc;
+    g.ldo2 = pl.ld_t;
     g.out_rows = nr64;
     g.out_cols = (int)pl.V_pad;
     g.lse = lse + r0;
@@ -339,15 +352,15 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     KD_TRY(launch("scatter", 0.0, (double)nr * pl.K * (8.0 + 4.0 * es), st, [&] {
       if (pl.vdt == KD_BF16)
         hipLaunchKernelGGL((scatter_kernel<T, bf16_t>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
-                           (const bf16_t*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.V_pad,
-                           dzt, pl.Nc);
+                           (const bf16_t*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.ld_v,
+                           dzt, pl.ld_t);
       else
         hipLaunchKernelGGL((scatter_kernel<T, float>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
-                           (const float*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.V_pad,
-                           dzt, pl.Nc);
+                           (const float*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.ld_v,
+                           dzt, pl.ld_t);
     }));
     // dH = dZ W  (P[t][j] = sum_v dZ[t][v] W^T[j][v])
-    GemmArgs gh = gemm_args(dz, pl.V_pad, nr, wt, pl.V_pad, (int)pl.d, (int)pl.V_pad);
+    GemmArgs gh = gemm_args(dz, pl.ld_v, nr, wt, pl.ld_v, (int)pl.d, (int)pl.V_pad);
     gh.out_rows = nr;
     gh.out_cols = (int)pl.d;
     gh.ldo = pl.d;
@@ -359,7 +372,7 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
       KD_TRY((run_gemm<T, EPI_STORE_BF16>("gemm_dh", gh, 2 * nr * pl.d, st)));
     }
     // dW (+)= dZ^T H  (P[v][j] = sum_t dZ^T[v][t] H^T[j][t])
-    GemmArgs gw = gemm_args(dzt, pl.Nc, (int)pl.V, ht, pl.Nc, (int)pl.d, nr64);
+    GemmArgs gw = gemm_args(dzt, pl.ld_t, (int)pl.V, ht, pl.ld_t, (int)pl.d, nr64);
     gw.out = dw;
     gw.ldo = pl.d;
     gw.out_rows = (int)pl.V;
@@ -394,12 +407,12 @@ kd_status topk_impl(const Plan& pl, const Layout& L, const void* ht, const void*
     const T* hc = (const T*)ht + r0 * pl.d;
     GemmArgs g = gemm_args(hc, pl.d, nr, wt, pl.d, (int)pl.V, (int)pl.d);
     g.out = S;
-    g.ldo = pl.V_pad;
+    g.ldo = pl.ld_v;
     g.out_rows = nr;
     g.out_cols = (int)pl.V_pad;
     KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_topk", g, 4 * nr * pl.V_pad, st)));
     KD_TRY(launch("topk_select", 0.0, 12.0 * nr * pl.V_pad + (double)nr * pl.K * (4 + sizeof(VT)), st, [&] {
-      hipLaunchKernelGGL((topk_select_kernel<T, VT>), dim3(nr), dim3(SEL_THREADS), 0, st, S, pl.V_pad, (int)pl.V,
+      hipLaunchKernelGGL((topk_select_kernel<T, VT>), dim3(nr), dim3(SEL_THREADS), 0, st, S, pl.ld_v, (int)pl.V,
                          pl.K, hc, (int)pl.d, (const T*)wt, wmax, idx + r0 * pl.K, (VT*)val + r0 * pl.K, overflow);
     }));
   }

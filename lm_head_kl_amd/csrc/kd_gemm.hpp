@@ -10,15 +10,17 @@
 //
 // Main loop (one workgroup per BX x BY output tile, 8 waves of 64 x 128 outputs):
 //  * operands reach LDS through wave-wide buffer loads that write LDS directly
-//    (no staging registers, no ds_write); rows past an operand's end and K past
-//    its end read as zero (out-of-range buffer offsets), so tails need no branches;
-//  * LDS holds NS = 5 stages of 64 bytes of K per row; the load of stage kt + 4 is
-//    issued while stage kt is multiplied, so a load has three stages of MFMA work
-//    to land; one barrier per stage;
-//  * the 16-byte chunks of each LDS row are XOR-swizzled by (row / 2) % 4, which
-//    makes the MFMA fragment reads (ds_read_b128, lane = row l % 16, chunk l / 16)
-//    free of bank conflicts on gfx950 (measured: 4 LDS cycles per read);
-//  * the fragments of stage kt + 1 are read from LDS during the MFMAs of stage kt;
+//    (no staging registers, no ds_write), each lane 16 bytes, 8 lanes per 128-byte
+//    row segment; rows past an operand's end and K past its end read as zero
+//    (out-of-range buffer offsets), so tails need no branches;
+//  * LDS holds 2 stages of 128 bytes of K per row (64 bf16 / 32 fp32); the load of
+//    stage kt + 2 is issued right after the barrier that frees stage kt's buffer;
+//  * each stage is two 64-byte MFMA fragments; the fragments of the next half are
+//    always read from LDS while the MFMAs of the current half run (one barrier per
+//    stage, placed between the halves);
+//  * the 16-byte chunks of each LDS row are XOR-swizzled by row % 8, which makes the
+//    fragment reads (ds_read_b128, lane = row l % 16, chunk l / 16) free of bank
+//    conflicts on gfx950 (measured: 4 LDS cycles per read, 256 B/clk);
 //  * bf16 uses v_mfma_f32_16x16x32_bf16; fp32 uses four v_mfma_f32_16x16x4_f32 on
 //    the same 16-byte fragment.
 //
@@ -33,7 +35,7 @@
 
 namespace kd {
 
-template <int BX_, int BY_, int WAVES_X_, int WAVES_Y_, int KB_, int NS_>
+template <int BX_, int BY_, int WAVES_X_, int WAVES_Y_>
 struct GemmCfg {
   static constexpr int BX = BX_, BY = BY_;
   static constexpr int WAVES_X = WAVES_X_, WAVES_Y = WAVES_Y_;
@@ -41,23 +43,21 @@ struct GemmCfg {
   static constexpr int NTHREADS = 64 * NWAVES;
   static constexpr int WX = BX / WAVES_X, WY = BY / WAVES_Y;
   static constexpr int FX = WX / 16, FY = WY / 16;
-  static constexpr int KB = KB_;                        // K bytes per row per stage
+  static constexpr int KB = 128;                        // K bytes per row per stage
   static constexpr int CPR = KB / 16;                   // 16-byte chunks per row
   static constexpr int STAGE_BYTES = (BX + BY) * KB;
-  static constexpr int NS = NS_;                        // LDS stages
-  static constexpr int MAIN_LDS = NS * STAGE_BYTES;
+  static constexpr int MAIN_LDS = 2 * STAGE_BYTES;
   static constexpr int DMA_PER_WAVE = STAGE_BYTES / 1024 / NWAVES;   // 1 KB wave-wide loads per stage
-  static_assert(NS >= 4 && STAGE_BYTES % (1024 * NWAVES) == 0 && (BX * KB) % 1024 == 0, "DMA blocks");
+  static_assert(STAGE_BYTES % (1024 * NWAVES) == 0 && (BX * KB) % 1024 == 0, "DMA blocks");
   static_assert((BX * KB / 1024) % DMA_PER_WAVE == 0, "a wave's blocks are all X or all Y");
-  static_assert(KB == 64, "one 16x16x32 fragment (64 bytes of K) per row per stage");
   static_assert(WX % 16 == 0 && WY % 64 == 0, "wave tile");
   // chunk swizzle of LDS row r (conflict-free ds_read_b128 fragment reads)
-  __device__ __forceinline__ static int swz(int r) { return (r >> 1) & 3; }
+  __device__ __forceinline__ static int swz(int r) { return r & 7; }
 };
 
 // The library's configuration: 256 x 256 tiles, 8 waves (4 along X, 2 along Y),
-// 64 x 128 outputs per wave, 64-byte K stages, 5 LDS stages (160 KiB).
-typedef GemmCfg<256, 256, 4, 2, 64, 5> MainCfg;
+// 64 x 128 outputs per wave (2 x 64 KiB LDS stages).
+typedef GemmCfg<256, 256, 4, 2> MainCfg;
 
 constexpr int BX = MainCfg::BX, BY = MainCfg::BY;
 
@@ -197,16 +197,19 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
 #pragma unroll
     for (int j = 0; j < FY; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane fragment read offsets (fragment rows start at multiples of 16, so the
-  // swizzle depends only on lane % 16)
+  // per-lane fragment read offsets of the two 64-byte halves of a stage row
+  // (fragment rows start at multiples of 16, so the swizzle depends on lane % 16)
   const int fr = lane & 15, fq = lane >> 4;
-  const uint32_t xs = uint32_t((wx * WX + fr) * C::KB + ((fq ^ C::swz(fr)) * 16));
-  const uint32_t ys = uint32_t((BXc + wy * WY + fr) * C::KB + ((fq ^ C::swz(fr)) * 16));
+  uint32_t xs[2], ys[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int ch = (f * 4 + fq) ^ C::swz(fr);
+    xs[f] = uint32_t((wx * WX + fr) * C::KB + ch * 16);
+    ys[f] = uint32_t((BXc + wy * WY + fr) * C::KB + ch * 16);
+  }
   const int nk = (a.k + KE - 1) / KE;
   {
-    // ---- LDS-DMA pipeline: stage s lives in LDS buffer s % NS; the DMA for stage
-    // kt + NS - 1 is issued in iteration kt, and the fragments of stage kt + 1 are
-    // read from LDS while the MFMAs of stage kt run.
+    // ---- LDS-DMA pipeline.  Stage kt lives in LDS buffer kt % 2.
     constexpr int DPW = C::DMA_PER_WAVE;
     constexpr int RPB = 1024 / C::KB;                    // rows per 1 KB DMA block
     constexpr int XBLK = BXc * C::KB / 1024;             // X blocks per stage
@@ -227,44 +230,43 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
       voff[q] = uint32_t(row * (isx ? a.ldx : a.ldy) * ES + ch * 16);
     }
     const bool wave_x = wave * DPW < XBLK;               // a wave's blocks are all X or all Y
-    auto issue = [&](int stage) {
+    auto issue = [&](int stage, int buf) {
       const int k0 = stage * KE;
-      const int buf = stage % C::NS;
 #pragma unroll
       for (int q = 0; q < DPW; ++q) {
         const uint32_t o = (k0 + vch[q] < a.k) ? voff[q] + uint32_t(k0 * ES) : kOOB;
         dma16(lds_base + uint32_t(buf * C::STAGE_BYTES + (wave * DPW + q) * 1024), o, wave_x ? xd : yd);
       }
     };
-    auto rdfrag = [&](u32x4 (&bx)[FX], u32x4 (&by)[FY], int stage) {
-      const char* base = lds + (stage % C::NS) * C::STAGE_BYTES;
+    auto rdfrag = [&](u32x4 (&bx)[FX], u32x4 (&by)[FY], int buf, int f) {
+      const char* base = lds + buf * C::STAGE_BYTES;
 #pragma unroll
-      for (int i = 0; i < FX; ++i) bx[i] = *(const u32x4*)(base + xs + i * 16 * C::KB);
+      for (int i = 0; i < FX; ++i) bx[i] = *(const u32x4*)(base + xs[f] + i * 16 * C::KB);
 #pragma unroll
-      for (int j = 0; j < FY; ++j) by[j] = *(const u32x4*)(base + ys + j * 16 * C::KB);
+      for (int j = 0; j < FY; ++j) by[j] = *(const u32x4*)(base + ys[f] + j * 16 * C::KB);
     };
-#pragma unroll
-    for (int s = 0; s < C::NS - 1; ++s) issue(s);
-    wait_vmcnt<DPW * (C::NS - 2)>();
-    __syncthreads();
-    u32x4 fa_x[FX], fa_y[FY], fb_x[FX], fb_y[FY];
-    auto step = [&](int kt, u32x4 (&cx)[FX], u32x4 (&cy)[FY], u32x4 (&nx_)[FX], u32x4 (&ny_)[FY]) {
-      wait_vmcnt<DPW * (C::NS - 3)>();                 // own loads of stage kt + 1 have landed
-      __syncthreads();                                   // everyone's; and buffer (kt-1) % NS is free
-      issue(kt + C::NS - 1);
-      rdfrag(nx_, ny_, kt + 1);
+    auto mma = [&](const u32x4 (&bx)[FX], const u32x4 (&by)[FY]) {
 #pragma unroll
       for (int i = 0; i < FX; ++i)
 #pragma unroll
-        for (int j = 0; j < FY; ++j) Mma<T>::run(acc[i][j], cy[j], cx[i]);
+        for (int j = 0; j < FY; ++j) Mma<T>::run(acc[i][j], by[j], bx[i]);
     };
-    rdfrag(fa_x, fa_y, 0);
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, fa_x, fa_y, fb_x, fb_y);
-      step(kt + 1, fb_x, fb_y, fa_x, fa_y);
+    issue(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    issue(1, 1);
+    u32x4 h0x[FX], h0y[FY], h1x[FX], h1y[FY];
+    rdfrag(h0x, h0y, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      rdfrag(h1x, h1y, cur, 1);          // second half of stage kt
+      mma(h0x, h0y);                     // first half of stage kt
+      wait_vmcnt<0>();                   // own loads of stage kt + 1 have landed
+      __syncthreads();                   // everyone's; every read of stage kt is done
+      issue(kt + 2, cur);                // stage kt + 2 into stage kt's buffer (zeros past the end)
+      rdfrag(h0x, h0y, cur ^ 1, 0);      // first half of stage kt + 1
+      mma(h1x, h1y);                     // second half of stage kt
     }
-    if (kt < nk) step(kt, fa_x, fa_y, fb_x, fb_y);
     wait_vmcnt<0>();
     __syncthreads();
   }

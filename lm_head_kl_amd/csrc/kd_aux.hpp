@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(256) transpose_pad_kernel(const T* __restrict_
 
 // ---------------------------------------------------------------------------
 // Subtract the scaled teacher probabilities at the cached entries of each row
-// from dZ and dZ^T.  One thread owns one row, so repeated indices within a row
+// from dZ (and from dZ^T when that copy exists).  One thread owns one row, so repeated indices within a row
 // are applied in k order with no race.
 template <typename T, typename VT>
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ idx, const VT* __restrict__ val,
@@ -197,8 +197,10 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
     const float pe = scale * expf(to_f32<VT>(vr[k]) * inv_tau - vmax - logZ);
     T* a = dz + (int64_t)t * ldz + v;
     *a = from_f32<T>(to_f32<T>(*a) - pe);
-    T* b = dzt + (int64_t)v * ldzt + t;
-    *b = from_f32<T>(to_f32<T>(*b) - pe);
+    if (dzt) {
+      T* b = dzt + (int64_t)v * ldzt + t;
+      *b = from_f32<T>(to_f32<T>(*b) - pe);
+    }
   }
 }
 

@@ -23,6 +23,16 @@
 //    conflicts on gfx950 (measured: 4 LDS cycles per read, 256 B/clk);
 //  * bf16 uses v_mfma_f32_16x16x32_bf16; fp32 uses four v_mfma_f32_16x16x4_f32 on
 //    the same 16-byte fragment.
+//  * K-major operands (bf16 only): an operand stored as [k][n] (n contiguous) is read
+//    with ds_read_b64_tr_b16.  Within each 16-lane group, output lane j, element e
+//    comes from input lane 4e + j/4, element j % 4 (measured), so input lane 4e + q
+//    pointing at k-row k0 + e, columns n0 + 4q .. n0 + 4q + 3 delivers rows k0..k0+3 of
+//    column n0 + j to lane j; two such reads (k0 and k0 + 4) make one MFMA fragment.
+//    The stage is laid out in 256-byte blocks, each holding 8 k-rows x 32 bytes of
+//    one 16-column fragment, so a read's bank position depends on the lane alone
+//    (the 32 lanes of a half-wave cover all 32 eight-byte bank slots) and fragment,
+//    k-half and row-half are immediate offsets.  This feeds dH = dZ W and
+//    dW = dZ^T H straight from dZ, W and H with no transposed copies.
 //
 // MFMA 16x16 lane layout: operand lane l supplies row (l % 16) and the 16-byte K
 // slice (l / 16); result lane l holds column n = l % 16 and rows m = 4(l/16)+e.
@@ -82,6 +92,7 @@ struct GemmArgs {
   const void* Y; int64_t ldy;     // [ny][k]
   int nx, ny, k;                  // valid rows of X and Y; contraction length
   int n_tx, n_ty, group;          // tile grid and tile-order grouping
+  int krows_x, krows_y;           // K-major operands: rows of k that exist (rows past them read as 0)
   // plain stores / dZ buffers
   void* out; int64_t ldo;         // P rows
   void* out2; int64_t ldo2;       // dZ^T rows (EPI_KL_DZ)
@@ -151,6 +162,8 @@ constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any operand: load
 // One wave-wide 16-byte-per-lane buffer load written straight into LDS: lane i's
 // data lands at LDS byte address lds_addr + 16 i (lds_addr wave-uniform).  It has no
 // destination register; completion is tracked with s_waitcnt vmcnt by the caller.
+// Every offset that selects rows goes through voff or the descriptor (both are
+// range-checked against the descriptor's size); the scalar offset stays 0.
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const u32x4& rsrc) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
@@ -174,8 +187,10 @@ __device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
   return r;
 }
 
-template <class C, typename T, int EPI>
+template <class C, typename T, int EPI, int XKM = 0, int YKM = 0>
 __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) {
+  static_assert(!(XKM || YKM) || (sizeof(T) == 2 && C::BX == 256 && C::BY == 256),
+                "K-major operands: bf16, 512-byte k rows");
   __shared__ __attribute__((aligned(16))) char lds[kernel_lds<C, EPI>()];
   constexpr int ES = int(sizeof(T));
   constexpr int EPC = 16 / ES;            // elements per 16-byte chunk
@@ -214,36 +229,84 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
     constexpr int RPB = 1024 / C::KB;                    // rows per 1 KB DMA block
     constexpr int XBLK = BXc * C::KB / 1024;             // X blocks per stage
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    const u32x4 xd = buffer_desc((const T*)a.X + (int64_t)x0 * a.ldx, (uint32_t)(xrows * a.ldx * ES));
-    const u32x4 yd = buffer_desc((const T*)a.Y + (int64_t)y0 * a.ldy, (uint32_t)(yrows * a.ldy * ES));
-    // block b of a stage: rows b*RPB .. of X (b < XBLK) or of Y; lane -> (row, swizzled chunk)
-    uint32_t voff[DPW];
-    int vch[DPW];
-    const int brow = lane / C::CPR, bp = lane % C::CPR;
-#pragma unroll
-    for (int q = 0; q < DPW; ++q) {
-      const int b = wave * DPW + q;
-      const bool isx = b < XBLK;
-      const int row = (isx ? b : b - XBLK) * RPB + brow;
-      const int ch = bp ^ C::swz(row);
-      vch[q] = ch * EPC;
-      voff[q] = uint32_t(row * (isx ? a.ldx : a.ldy) * ES + ch * 16);
-    }
+    // block b of a stage: rows b*RPB .. of X (b < XBLK) or of Y
     const bool wave_x = wave * DPW < XBLK;               // a wave's blocks are all X or all Y
+    const bool wave_km = wave_x ? (XKM != 0) : (YKM != 0);
+    const int bl0 = wave * DPW - (wave_x ? 0 : XBLK);    // first block of this wave in its operand
+    const int64_t ld = wave_x ? a.ldx : a.ldy;
+    const uint32_t ldb = uint32_t(ld * ES);              // operand row stride in bytes
+    const int col0 = wave_x ? x0 : y0;
+    const char* opb = (const char*)(wave_x ? a.X : a.Y); // operand base
+    const uint32_t op_rows = uint32_t(wave_x ? xrows : yrows);
+    const int krows = wave_x ? a.krows_x : a.krows_y;
+    // Row-major: block = RPB rows x 128 bytes; lane -> (row, swizzled 16-byte chunk),
+    // one offset per block from the tile's descriptor (rows past the tile's valid
+    // rows fall outside it and read as 0)
+    const u32x4 od = buffer_desc(opb + (int64_t)col0 * ld * ES, op_rows * ldb);
+    const int lrow = lane / C::CPR;
+    const int lch = (lane % C::CPR) ^ C::swz(lrow);      // RPB = 8: the swizzle depends on the lane alone
+    const int kq = lch * EPC;                            // first k element of this lane's chunk
+    uint32_t voff[DPW];
+#pragma unroll
+    for (int q = 0; q < DPW; ++q) voff[q] = uint32_t(((bl0 + q) * RPB + lrow) * ldb + lch * 16);
+    // K-major: a stage of an operand is 64 k-rows x 256 columns (32 KB).  LDS byte
+    //   1024 m + 256 b + 128 r1 + 32 e + 16 c + 8 hf   holds k-row
+    //   16 (m & 1) + 8 r1 + e + 4 ((m >> 3) & 1) + 32 (m >> 4),  columns
+    //   16 (b + 4 ((m >> 1) & 3)) + 8 c + 4 hf + 0..3,
+    // i.e. fragment G = b + 4 ((m >> 1) & 3) (16 columns), k-half f = m >> 4,
+    // k-quad h = (m >> 3) & 1 and rows 8 g + e with g = 2 (m & 1) + r1.  DMA m writes
+    // the 1 KB at 1024 m; its lane L covers b = L / 16, r1 = (L / 8) & 1,
+    // e = (L / 2) & 3, c = L & 1, which in the operand is rows 8 r1 + e and bytes
+    // 32 b + 16 c past the DMA's first row and column.
+    const uint32_t voff_km = uint32_t((8 * ((lane >> 3) & 1) + ((lane >> 1) & 3)) * ldb +
+                                      (2 * (lane >> 4) + (lane & 1)) * 16);
     auto issue = [&](int stage, int buf) {
       const int k0 = stage * KE;
+      const uint32_t ldsb = lds_base + uint32_t(buf * C::STAGE_BYTES + wave * DPW * 1024);
+      if (wave_km) {
+        // rows past krows fall outside the descriptor and read as 0
+        const int rows = krows - k0;
 #pragma unroll
-      for (int q = 0; q < DPW; ++q) {
-        const uint32_t o = (k0 + vch[q] < a.k) ? voff[q] + uint32_t(k0 * ES) : kOOB;
-        dma16(lds_base + uint32_t(buf * C::STAGE_BYTES + (wave * DPW + q) * 1024), o, wave_x ? xd : yd);
+        for (int q = 0; q < DPW; ++q) {
+          const int m = bl0 + q;
+          const int r0 = 16 * (m & 1) + 4 * ((m >> 3) & 1) + 32 * (m >> 4);
+          const int64_t cb = (int64_t)col0 * ES + 128 * ((m >> 1) & 3);
+          const int64_t nb = (int64_t)(rows - r0) * ldb - cb;
+          const u32x4 d = buffer_desc(opb + (int64_t)(k0 + r0) * ldb + cb,
+                                      (rows > r0 && nb > 0) ? uint32_t(nb) : 0u);
+          dma16(ldsb + q * 1024, voff_km, d);
+        }
+      } else {
+        // chunks at or past k read as 0
+        const bool kin = k0 + kq < a.k;
+#pragma unroll
+        for (int q = 0; q < DPW; ++q) dma16(ldsb + q * 1024, kin ? voff[q] + uint32_t(k0 * ES) : kOOB, od);
       }
+    };
+    // K-major fragment G of k-half f: lane 16 g + 4 e + q reads k-rows 8 g + e (+4)
+    // at columns 16 G + 4 q; lane part of the address, the rest are immediates
+    const uint32_t trb = uint32_t(1024 * (lane >> 5) + 128 * ((lane >> 4) & 1) + 32 * ((lane >> 2) & 3) +
+                                  8 * (lane & 3));
+    auto trfrag = [&](const char* region, int G, int f) {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      const char* p = region + trb + 256 * (G & 3) + 2048 * (G >> 2) + 16384 * f;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 8192));
+      const u32x2 a0 = __builtin_bit_cast(u32x2, lo), a1 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{a0[0], a0[1], a1[0], a1[1]};
     };
     auto rdfrag = [&](u32x4 (&bx)[FX], u32x4 (&by)[FY], int buf, int f) {
       const char* base = lds + buf * C::STAGE_BYTES;
 #pragma unroll
-      for (int i = 0; i < FX; ++i) bx[i] = *(const u32x4*)(base + xs[f] + i * 16 * C::KB);
+      for (int i = 0; i < FX; ++i) {
+        if constexpr (XKM) bx[i] = trfrag(base, (wx * WX) / 16 + i, f);
+        else bx[i] = *(const u32x4*)(base + xs[f] + i * 16 * C::KB);
+      }
 #pragma unroll
-      for (int j = 0; j < FY; ++j) by[j] = *(const u32x4*)(base + ys[f] + j * 16 * C::KB);
+      for (int j = 0; j < FY; ++j) {
+        if constexpr (YKM) by[j] = trfrag(base + BXc * C::KB, (wy * WY) / 16 + j, f);
+        else by[j] = *(const u32x4*)(base + ys[f] + j * 16 * C::KB);
+      }
     };
     auto mma = [&](const u32x4 (&bx)[FX], const u32x4 (&by)[FY]) {
 #pragma unroll
@@ -384,8 +447,10 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
         for (int e = 0; e < 4; ++e)
           v[e] = (rv && m + e < a.ny) ? scale * fast_exp2(fmaf(acc[i][j][e], kLog2e, nl)) : 0.f;
         store4<T>(dz + (int64_t)n * a.ldo + m, v);
+        if (dzt) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dzt[(int64_t)(m + e) * a.ldo2 + n] = from_f32<T>(v[e]);
+          for (int e = 0; e < 4; ++e) dzt[(int64_t)(m + e) * a.ldo2 + n] = from_f32<T>(v[e]);
+        }
       }
     }
   }

@@ -122,7 +122,9 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     L->wt = take((size_t)(pl.esz * pl.d * pl.ld_v));
     L->ht = take((size_t)(pl.esz * pl.d * pl.ld_t));
     L->dz = take((size_t)(pl.esz * pl.Nc * pl.ld_v));
-    L->dzt = take((size_t)(pl.esz * pl.V_pad * pl.ld_t));
+    // bf16 reads dZ K-major in the dW product; float32 (no transposing LDS read)
+    // keeps a transposed copy
+    if (pl.xdt == KD_F32) L->dzt = take((size_t)(pl.esz * pl.V_pad * pl.ld_t));
   } else {
     L->s = take(sizeof(float) * (size_t)(pl.Nc * pl.ld_v));
     L->bmax = take(sizeof(double) * 1024);
@@ -234,14 +236,14 @@ GemmArgs gemm_args(const void* X, int64_t ldx, int nx, const void* Y, int64_t ld
   return g;
 }
 
-template <typename T, int EPI>
+template <typename T, int EPI, int XKM = 0, int YKM = 0>
 kd_status run_gemm(const char* kind, const GemmArgs& g, int64_t out_bytes, hipStream_t st) {
   if (g.nx <= 0 || g.ny <= 0) return KD_OK;
   const unsigned blocks = (unsigned)(g.n_tx * g.n_ty);
   const double flops = 2.0 * g.nx * (double)g.ny * g.k;
   const double bytes = (double)sizeof(T) * ((double)g.nx + g.ny) * g.k + (double)out_bytes;
   return launch(kind, flops, bytes, st, [&] {
-    hipLaunchKernelGGL((gemm_kernel<MainCfg, T, EPI>), dim3(blocks), dim3(MainCfg::NTHREADS), 0, st, g);
+    hipLaunchKernelGGL((gemm_kernel<MainCfg, T, EPI, XKM, YKM>), dim3(blocks), dim3(MainCfg::NTHREADS), 0, st, g);
   });
 }
 
@@ -314,10 +316,14 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
                    const void* val, const float* lse, const float* grad, void* dh, float* dw, char* ws,
                    hipStream_t st) {
   if (pl.N == 0) return zero_words(dw, pl.V * pl.d, st);
+  // W^T and H^T are cheap copies (W once, H per chunk).  dZ^T would cost a second
+  // N x V write per chunk: bf16 reads dZ K-major in the dW product instead
+  // (transposing LDS reads); float32 writes dZ^T from the dZ epilogue.
+  constexpr bool kKm = std::is_same<T, bf16_t>::value;
   T* wt = (T*)(ws + L.wt);
   T* ht = (T*)(ws + L.ht);
   T* dz = (T*)(ws + L.dz);
-  T* dzt = (T*)(ws + L.dzt);
+  T* dzt = kKm ? nullptr : (T*)(ws + L.dzt);
   const float inv_n = 1.0f / (float)pl.N;
   const float inv_tau = 1.0f / pl.tau;
   const int64_t es = (int64_t)sizeof(T);
@@ -346,10 +352,10 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     g.lse = lse + r0;
     g.grad = grad;
     g.inv_n = inv_n;
-    KD_TRY((run_gemm<T, EPI_KL_DZ>("gemm_dz", g, 2 * es * nr * pl.V, st)));
+    KD_TRY((run_gemm<T, EPI_KL_DZ>("gemm_dz", g, (kKm ? 1 : 2) * es * nr * pl.V, st)));
     // subtract the teacher at the cached entries
     const int nb = (int)cdiv(nr, 256);
-    KD_TRY(launch("scatter", 0.0, (double)nr * pl.K * (8.0 + 4.0 * es), st, [&] {
+    KD_TRY(launch("scatter", 0.0, (double)nr * pl.K * (8.0 + (kKm ? 2.0 : 4.0) * es), st, [&] {
       if (pl.vdt == KD_BF16)
         hipLaunchKernelGGL((scatter_kernel<T, bf16_t>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
                            (const bf16_t*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.ld_v,
@@ -371,14 +377,16 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
       gh.out = (bf16_t*)dh + r0 * pl.d;
       KD_TRY((run_gemm<T, EPI_STORE_BF16>("gemm_dh", gh, 2 * nr * pl.d, st)));
     }
-    // dW (+)= dZ^T H  (P[v][j] = sum_t dZ^T[v][t] H^T[j][t])
-    GemmArgs gw = gemm_args(dzt, pl.ld_t, (int)pl.V, ht, pl.ld_t, (int)pl.d, nr64);
+    // dW (+)= dZ^T H  (P[v][j] = sum_t dZ[t][v] H^T[j][t]; bf16 reads X = dZ K-major)
+    GemmArgs gw = kKm ? gemm_args(dz, pl.ld_v, (int)pl.V, ht, pl.ld_t, (int)pl.d, nr64)
+                      : gemm_args(dzt, pl.ld_t, (int)pl.V, ht, pl.ld_t, (int)pl.d, nr64);
+    gw.krows_x = nr;
     gw.out = dw;
     gw.ldo = pl.d;
     gw.out_rows = (int)pl.V;
     gw.out_cols = (int)pl.d;
     gw.accumulate = r0 > 0;
-    KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_dw", gw, (r0 > 0 ? 8 : 4) * pl.V * pl.d, st)));
+    KD_TRY((run_gemm<T, EPI_STORE_F32, kKm, 0>("gemm_dw", gw, (r0 > 0 ? 8 : 4) * pl.V * pl.d, st)));
   }
   return KD_OK;
 }

@@ -5,7 +5,8 @@
 // with P stored row-major, so one lane writes 4 consecutive m of one row n:
 //   logits   Z[t][v]  : X = H rows (tokens),     Y = W rows (vocabulary), K = d
 //   dH[t][j]          : X = dZ rows (tokens),    Y = W^T rows (hidden),   K = V
-//   dW[v][j]          : X = dZ^T rows (vocab),   Y = H^T rows (hidden),   K = tokens
+//   dW[v][j]          : X = dZ read K-major (bf16) or dZ^T rows (fp32),
+//                       Y = H^T rows (hidden),   K = tokens
 //   teacher S[t][v]   : X = H_T rows,            Y = W_T rows,            K = d
 //
 // Main loop (one workgroup per BX x BY output tile, 8 waves of 64 x 128 outputs):
@@ -31,8 +32,9 @@
 //    The stage is laid out in 256-byte blocks, each holding 8 k-rows x 32 bytes of
 //    one 16-column fragment, so a read's bank position depends on the lane alone
 //    (the 32 lanes of a half-wave cover all 32 eight-byte bank slots) and fragment,
-//    k-half and row-half are immediate offsets.  This feeds dH = dZ W and
-//    dW = dZ^T H straight from dZ, W and H with no transposed copies.
+//    k-half and row-half are immediate offsets (measured: 1.8x faster than 512-byte
+//    XOR-swizzled k-rows).  The dW product reads dZ this way, so no N x V transposed
+//    copy of dZ is ever written.
 //
 // MFMA 16x16 lane layout: operand lane l supplies row (l % 16) and the 16-byte K
 // slice (l / 16); result lane l holds column n = l % 16 and rows m = 4(l/16)+e.

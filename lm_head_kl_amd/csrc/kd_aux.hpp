@@ -278,7 +278,8 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, int need, int* 
   __syncthreads();
 }
 
-// Exact top-K of one teacher row.  s[V] holds the float32 MFMA logits.
+// Exact top-K of one teacher row (general path; with rows_todo, only the rows the
+// fast path below handed over).  s[V] holds the float32 MFMA logits.
 //  1. Two 12-bit radix histograms of the order-preserving key locate a
 //     sub-bin [lo, ...) that contains the K-th largest float32 value T_K.
 //  2. Every value >= lo - 2*eps is a candidate, where eps bounds |fp32 - exact|
@@ -290,7 +291,8 @@ template <typename T, typename VT>
 __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
     const float* __restrict__ S, int64_t ld_s, int V, int K, const T* __restrict__ ht, int d,
     const T* __restrict__ wt, const double* __restrict__ wmax, int32_t* __restrict__ idx_out,
-    VT* __restrict__ val_out, int* __restrict__ overflow) {
+    VT* __restrict__ val_out, int* __restrict__ overflow, const int* __restrict__ rows_todo) {
+  if (rows_todo && !rows_todo[blockIdx.x]) return;   // handled by topk_select_fast_kernel
   __shared__ uint32_t hist[4096];
   __shared__ int cidx[SEL_CAP];
   __shared__ double cscore[SEL_CAP];
@@ -382,6 +384,122 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
       else val_out[(int64_t)row * K + rank] = (float)sc;
     }
   }
+}
+
+// Exact top-K of one teacher row, fast path.  The GEMM epilogue left, for every
+// 256-column vocabulary tile, the row's two largest float32 logits in the tile.
+//  1. Those 2 n_ty values are distinct elements of the row, so their K-th largest
+//     t is <= the row's K-th largest float32 logit (bitwise search over the
+//     order-preserving keys, 32 block counts).
+//  2. One pass over the row keeps every logit >= t - 2 eps (eps as in the general
+//     path): the exact top-K are all among them.
+//  3. float64 re-scoring, ranking by (score desc, index asc), first K written.
+// A row this path cannot take (2 n_ty < K, more tile values than TOPS_CAP, more
+// candidates than FAST_CAP) is flagged in rows_todo for the general kernel.
+constexpr int TOPS_CAP = 4096;
+constexpr int FAST_CAP = 1536;
+template <typename T, typename VT>
+__global__ void __launch_bounds__(SEL_THREADS) topk_select_fast_kernel(
+    const float* __restrict__ S, int64_t ld_s, int V, int K, const float2* __restrict__ tops, int64_t ld_tops,
+    int n_ty, const T* __restrict__ ht, int d, const T* __restrict__ wt, const double* __restrict__ wmax,
+    int32_t* __restrict__ idx_out, VT* __restrict__ val_out, int* __restrict__ rows_todo) {
+  __shared__ uint32_t keys[TOPS_CAP];
+  __shared__ int cidx[FAST_CAP];
+  __shared__ double cscore[FAST_CAP];
+  __shared__ double shd[SEL_THREADS];
+  __shared__ int shc[SEL_THREADS / 64];
+  __shared__ int ncand;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = 2 * n_ty;
+  if (M < K || M > TOPS_CAP) {
+    if (tid == 0) rows_todo[row] = 1;
+    return;
+  }
+  for (int q = tid; q < n_ty; q += SEL_THREADS) {
+    const float2 t = tops[(int64_t)q * ld_tops + row];
+    keys[2 * q] = float_key(t.x);
+    keys[2 * q + 1] = float_key(t.y);
+  }
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  // 1. largest key t with #{keys >= t} >= K, i.e. the K-th largest key
+  uint32_t t = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    int n = 0;
+    for (int q = tid; q < M; q += SEL_THREADS) n += keys[q] >= c;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+    if (lane == 0) shc[wave] = n;
+    __syncthreads();
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < SEL_THREADS / 64; ++w) tot += shc[w];
+    __syncthreads();
+    if (tot >= K) t = c;
+  }
+  const float* s = S + (int64_t)row * ld_s;
+  const T* h = ht + (int64_t)row * d;
+  double hn = 0.0;
+  for (int j = tid; j < d; j += SEL_THREADS) {
+    const double x = (double)to_f32<T>(h[j]);
+    hn += x * x;
+  }
+  hn = sqrt(block_sum_256(hn, shd));
+  const double eps = 2.0 * (double)d * 0x1p-23 * hn * (*wmax);
+  const float thr = __double2float_rd((double)key_float(t) - 2.0 * eps);
+  // 2. candidates (V is a multiple of 4 or the tail is handled by the index test)
+  const int nq = (V + 3) / 4;
+  for (int q = tid; q < nq; q += SEL_THREADS) {
+    const f32x4 x = *(const f32x4*)(s + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 4 * q + e;
+      if (v < V && x[e] >= thr) {
+        const int pos = atomicAdd(&ncand, 1);
+        if (pos < FAST_CAP) cidx[pos] = v;
+      }
+    }
+  }
+  __syncthreads();
+  const int C = ncand;
+  if (C > FAST_CAP) {
+    if (tid == 0) rows_todo[row] = 1;
+    return;
+  }
+  // 3. float64 re-scoring: one wave per candidate, lanes split d in 16-byte chunks
+  constexpr int EPC = 16 / int(sizeof(T));
+  for (int c = wave; c < C; c += SEL_THREADS / 64) {
+    const T* w = wt + (int64_t)cidx[c] * d;
+    double acc = 0.0;
+    for (int j = lane * EPC; j < d; j += 64 * EPC) {
+      const u32x4 hv = *(const u32x4*)(h + j);
+      const u32x4 wv = *(const u32x4*)(w + j);
+      const T* hp = (const T*)&hv;
+      const T* wp = (const T*)&wv;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc = fma((double)to_f32<T>(hp[e]), (double)to_f32<T>(wp[e]), acc);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) cscore[c] = acc;
+  }
+  __syncthreads();
+  for (int c = tid; c < C; c += SEL_THREADS) {
+    const double sc = cscore[c];
+    const int vi = cidx[c];
+    int rank = 0;
+    for (int o = 0; o < C; ++o) {
+      const double so = cscore[o];
+      rank += (so > sc) || (so == sc && cidx[o] < vi);
+    }
+    if (rank < K) {
+      idx_out[(int64_t)row * K + rank] = vi;
+      if constexpr (sizeof(VT) == 2) val_out[(int64_t)row * K + rank] = f64_to_bf16_rne(sc);
+      else val_out[(int64_t)row * K + rank] = (float)sc;
+    }
+  }
+  if (tid == 0) rows_todo[row] = 0;
 }
 
 }  // namespace kd

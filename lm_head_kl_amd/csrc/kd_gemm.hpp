@@ -86,7 +86,8 @@ enum Epi : int {
   EPI_STORE_F32 = 0,   // P -> float out (optionally += existing)
   EPI_STORE_BF16 = 1,  // P -> bf16 out
   EPI_KL_FWD = 2,      // per-row online (max, sum exp) partials + cached-entry gather
-  EPI_KL_DZ = 3,       // dZ = (g/N) exp(z - lse) -> dZ and dZ^T buffers
+  EPI_KL_DZ = 3,       // dZ = (g/N) exp(z - lse) -> dZ (and, if given, dZ^T)
+  EPI_TOPK = 4,        // P -> float out, plus the two largest values of each row in the tile
 };
 
 struct GemmArgs {
@@ -108,7 +109,7 @@ struct GemmArgs {
   const int* offsets;             // [n_tx][n_ty + 1]
   int kc;                         // cache entries per row (K)
   float* zg;                      // [rows][K] gathered logits
-  float2* partials;               // [n_ty][ld_part] per-row (max, sum exp)
+  float2* partials;               // [n_ty][ld_part] per row: (max, sum exp) or (1st, 2nd largest)
   int64_t ld_part;
 };
 
@@ -340,8 +341,8 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
   const int nrow0 = x0 + wx * WX + (lane & 15);
   const int mcol = y0 + wy * WY + (lane >> 4) * 4;
 
-  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16) {
-    typedef typename std::conditional<EPI == EPI_STORE_F32, float, bf16_t>::type OT;
+  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16 || EPI == EPI_TOPK) {
+    typedef typename std::conditional<EPI == EPI_STORE_BF16, bf16_t, float>::type OT;
 #pragma unroll
     for (int i = 0; i < FX; ++i) {
       const int n = nrow0 + i * 16;
@@ -356,6 +357,46 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
           if (a.accumulate) v += *(const f32x4*)(orow + m);
         }
         store4<OT>(orow + m, v);
+      }
+    }
+    if constexpr (EPI == EPI_TOPK) {
+      // The two largest values of each row among the tile's valid columns: in-lane,
+      // then over the 4 lanes sharing the row, then over the waves along Y in LDS.
+      // Distinct elements of the row, so the K-th largest over all tiles' pairs
+      // bounds the row's K-th largest from below.
+      float2* st = (float2*)lds;   // the main loop's buffers are free after its last barrier
+#pragma unroll
+      for (int i = 0; i < FX; ++i) {
+        float a1 = -INFINITY, a2 = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < FY; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = acc[i][j][e];
+            if (mcol + j * 16 + e < a.ny) {
+              a2 = fmaxf(a2, fminf(a1, v));
+              a1 = fmaxf(a1, v);
+            }
+          }
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+          const float b1 = __shfl_xor(a1, o), b2 = __shfl_xor(a2, o);
+          a2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+          a1 = fmaxf(a1, b1);
+        }
+        if ((lane >> 4) == 0) st[wy * BXc + wx * WX + i * 16 + lane] = make_float2(a1, a2);
+      }
+      __syncthreads();
+      if (tid < BXc) {
+        float2 t = st[tid];
+#pragma unroll
+        for (int w = 1; w < C::WAVES_Y; ++w) {
+          const float2 b = st[w * BXc + tid];
+          t.y = fmaxf(fminf(t.x, b.x), fmaxf(t.y, b.y));
+          t.x = fmaxf(t.x, b.x);
+        }
+        const int row = x0 + tid;
+        if (row < a.nx) a.partials[(int64_t)ty * a.ld_part + row] = t;
       }
     }
   } else if constexpr (EPI == EPI_KL_FWD) {

@@ -55,7 +55,7 @@ struct Plan {
 struct Layout {
   size_t entries, offsets, zg, partials, block_sums, flags;       // forward
   size_t wt, ht, dz, dzt;                                         // backward
-  size_t s, bmax, wmax, overflow;                                 // cache build
+  size_t s, bmax, wmax, overflow, tops, todo;                     // cache build
   size_t total;
 };
 
@@ -130,6 +130,8 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     L->bmax = take(sizeof(double) * 1024);
     L->wmax = take(sizeof(double));
     L->overflow = take(sizeof(int) * 4);
+    L->tops = take(sizeof(float) * 2 * (size_t)(pl.n_ty * pl.Nc));
+    L->todo = take(sizeof(int) * (size_t)pl.Nc);
   }
   L->total = cur;
   return cur;
@@ -399,6 +401,8 @@ kd_status topk_impl(const Plan& pl, const Layout& L, const void* ht, const void*
   double* bmax = (double*)(ws + L.bmax);
   double* wmax = (double*)(ws + L.wmax);
   int* overflow = (int*)(ws + L.overflow);
+  float2* tops = (float2*)(ws + L.tops);
+  int* todo = (int*)(ws + L.todo);
   const bool check = debug_checks();
   if (check) KD_TRY(zero_words(overflow, 4, st));
   const int64_t es = (int64_t)sizeof(T);
@@ -418,10 +422,20 @@ kd_status topk_impl(const Plan& pl, const Layout& L, const void* ht, const void*
     g.ldo = pl.ld_v;
     g.out_rows = nr;
     g.out_cols = (int)pl.V_pad;
-    KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_topk", g, 4 * nr * pl.V_pad, st)));
-    KD_TRY(launch("topk_select", 0.0, 12.0 * nr * pl.V_pad + (double)nr * pl.K * (4 + sizeof(VT)), st, [&] {
+    g.partials = tops;
+    g.ld_part = pl.Nc;
+    KD_TRY((run_gemm<T, EPI_TOPK>("gemm_topk", g, 4 * nr * pl.V_pad, st)));
+    // one pass over each row's logits from the tile pairs' bound; rows it cannot take
+    // go to the general radix kernel
+    KD_TRY(launch("topk_select", 0.0, 4.0 * nr * pl.V_pad + (double)nr * pl.K * (4 + sizeof(VT)), st, [&] {
+      hipLaunchKernelGGL((topk_select_fast_kernel<T, VT>), dim3(nr), dim3(SEL_THREADS), 0, st, S, pl.ld_v,
+                         (int)pl.V, pl.K, (const float2*)tops, pl.Nc, pl.n_ty, hc, (int)pl.d, (const T*)wt, wmax,
+                         idx + r0 * pl.K, (VT*)val + r0 * pl.K, todo);
+    }));
+    KD_TRY(launch("topk_fallback", 0.0, 4.0 * nr, st, [&] {
       hipLaunchKernelGGL((topk_select_kernel<T, VT>), dim3(nr), dim3(SEL_THREADS), 0, st, S, pl.ld_v, (int)pl.V,
-                         pl.K, hc, (int)pl.d, (const T*)wt, wmax, idx + r0 * pl.K, (VT*)val + r0 * pl.K, overflow);
+                         pl.K, hc, (int)pl.d, (const T*)wt, wmax, idx + r0 * pl.K, (VT*)val + r0 * pl.K, overflow,
+                         (const int*)todo);
     }));
   }
   if (check) {

@@ -216,14 +216,16 @@ def random_cache(n_tokens: int, vocab: int, k: int, seed: int = 0, scale: float 
 
 
 def small_problem(n: int, d: int, v: int, seed: int, dtype: str = "bf16",
-                  teacher_noise: float = 0.5) -> Dict[str, np.ndarray]:
+                  teacher_noise: float = 0.5, logit_scale: float = 1.0) -> Dict[str, np.ndarray]:
     """Arbitrary small shapes (ragged tails etc.) with the workload recipe:
-    ``H ~ N(0,1)``, ``W ~ N(0,1/d)``, ``W_T = W + N(0, noise^2/d)``."""
+    ``H ~ N(0,1)``, ``W ~ N(0,1/d)``, ``W_T = W + N(0, noise^2/d)``.  ``logit_scale``
+    multiplies H before rounding (logits ~ N(0, scale^2): the stress variant for the
+    online max / rescaling)."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2026, 7, seed, n, d, v])))
     sc = np.float32(1.0 / np.sqrt(d))
     w32 = g.standard_normal((v, d), dtype=np.float32) * sc
     w = _store(w32, dtype)
     base = f32_from_bf16_bits(w) if dtype == "bf16" else w32
     wt = _store(base + g.standard_normal((v, d), dtype=np.float32) * np.float32(teacher_noise) * sc, dtype)
-    h = _store(g.standard_normal((n, d), dtype=np.float32), dtype)
+    h = _store(g.standard_normal((n, d), dtype=np.float32) * np.float32(logit_scale), dtype)
     return {"H": h, "W": w, "WT": wt, "dtype": dtype}

@@ -249,9 +249,6 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
     const int lrow = lane / C::CPR;
     const int lch = (lane % C::CPR) ^ C::swz(lrow);      // RPB = 8: the swizzle depends on the lane alone
     const int kq = lch * EPC;                            // first k element of this lane's chunk
-    uint32_t voff[DPW];
-#pragma unroll
-    for (int q = 0; q < DPW; ++q) voff[q] = uint32_t(((bl0 + q) * RPB + lrow) * ldb + lch * 16);
     // K-major: a stage of an operand is 64 k-rows x 256 columns (32 KB).  LDS byte
     //   1024 m + 256 b + 128 r1 + 32 e + 16 c + 8 hf   holds k-row
     //   16 (m & 1) + 8 r1 + e + 4 ((m >> 3) & 1) + 32 (m >> 4),  columns
@@ -261,24 +258,30 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
     // the 1 KB at 1024 m; its lane L covers b = L / 16, r1 = (L / 8) & 1,
     // e = (L / 2) & 3, c = L & 1, which in the operand is rows 8 r1 + e and bytes
     // 32 b + 16 c past the DMA's first row and column.
+    // Per-block offsets, loop-invariant: row-major block q is rows (bl0 + q) RPB ..;
+    // K-major block m = bl0 + q starts at k-row r0(m) and byte cb(m) of the row.
     const uint32_t voff_km = uint32_t((8 * ((lane >> 3) & 1) + ((lane >> 1) & 3)) * ldb +
                                       (2 * (lane >> 4) + (lane & 1)) * 16);
+    uint32_t voff[DPW];
+#pragma unroll
+    for (int q = 0; q < DPW; ++q) {
+      const int m = bl0 + q;
+      const int r0 = 16 * (m & 1) + 4 * ((m >> 3) & 1) + 32 * (m >> 4);
+      voff[q] = wave_km ? voff_km + uint32_t(r0) * ldb + uint32_t(col0 * ES + 128 * ((m >> 1) & 3))
+                        : uint32_t((m * RPB + lrow) * ldb + lch * 16);
+    }
     auto issue = [&](int stage, int buf) {
       const int k0 = stage * KE;
       const uint32_t ldsb = lds_base + uint32_t(buf * C::STAGE_BYTES + wave * DPW * 1024);
       if (wave_km) {
-        // rows past krows fall outside the descriptor and read as 0
+        // one descriptor per stage from k-row k0, column 0 of the operand's rows: rows
+        // past krows, and bytes past the end of the last valid row, read as 0
         const int rows = krows - k0;
+        const int64_t nb = (int64_t)rows * ldb;
+        const u32x4 d = buffer_desc(opb + (int64_t)k0 * ldb,
+                                    rows > 0 ? uint32_t(nb < 0xffffffffll ? nb : 0xffffffffll) : 0u);
 #pragma unroll
-        for (int q = 0; q < DPW; ++q) {
-          const int m = bl0 + q;
-          const int r0 = 16 * (m & 1) + 4 * ((m >> 3) & 1) + 32 * (m >> 4);
-          const int64_t cb = (int64_t)col0 * ES + 128 * ((m >> 1) & 3);
-          const int64_t nb = (int64_t)(rows - r0) * ldb - cb;
-          const u32x4 d = buffer_desc(opb + (int64_t)(k0 + r0) * ldb + cb,
-                                      (rows > r0 && nb > 0) ? uint32_t(nb) : 0u);
-          dma16(ldsb + q * 1024, voff_km, d);
-        }
+        for (int q = 0; q < DPW; ++q) dma16(ldsb + q * 1024, voff[q], d);
       } else {
         // chunks at or past k read as 0
         const bool kin = k0 + kq < a.k;

@@ -80,6 +80,85 @@ def cpu_baseline(workload, n_rows: int, k: int):
                       f"float64 forward+backward, synthetic cache of the same shape; {dt:.1f} s"}
 
 
+def run_point(kd, torch, w, h, wd, wt, n, k, steps, warmup, chunk=0):
+    """Cache build (timed once) and `steps` timed fwd+bwd steps on the first n rows of h."""
+    hn = h[:n]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    idx, val = kd.kd_topk_cache_build(hn, wt, k)
+    e1.record()
+    torch.cuda.synchronize()
+    cache_ms = e0.elapsed_time(e1)
+    dh_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    torch.cuda.empty_cache()
+    # peak of this point alone: the step's own inputs (H rows, W, cache) plus everything
+    # the step allocates (outputs, workspace); other resident tensors are excluded
+    own = hn.numel() * hn.element_size() + wd.numel() * wd.element_size() + \
+        idx.numel() * idx.element_size() + val.numel() * val.element_size()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+
+    def step():
+        loss, lse, _ = kd.kd_chunked_kl_fwd(hn, wd, idx, val, w.tau, chunk_tokens=chunk)
+        dh, dw = kd.kd_chunked_kl_bwd(hn, wd, idx, val, w.tau, lse, None, dh_dtype=dh_dtype, chunk_tokens=chunk)
+        return loss
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        loss = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    peak_gb = (torch.cuda.max_memory_allocated() - base + own) / 1e9
+    flops = 8.0 * n * w.vocab * w.d
+    peak_tf = BF16_DENSE_PEAK_TFLOPS if w.dtype == "bf16" else FP32_DENSE_PEAK_TFLOPS
+    out = {"workload": w.name, "n_tokens": n, "d": w.d, "vocab": w.vocab, "k": k, "tau": w.tau,
+           "tokens_per_s": round(n / (ms / 1e3), 1), "ms_per_step": round(ms, 3),
+           "mfma_util": round(flops / (ms / 1e3) / (peak_tf * 1e12), 4), "peak_gb": round(peak_gb, 3),
+           "cache_build_ms": round(cache_ms, 2), "loss": round(loss.item(), 5)}
+    del idx, val
+    return out
+
+
+def sweep(kd, torch, np, kd_synth, steps, warmup):
+    points = [("seq4k_v32k", None), ("long32k_v201k", None), ("ctx32k_v128k", None), ("packed131k_v128k", None),
+              ("sweep_v128k", None)]
+    rows = []
+    for name, _ in points:
+        w = kd_synth.WORKLOADS[name]
+        dev = torch.device("cuda:0")
+
+        def to_dev(x):
+            if w.dtype == "bf16":
+                return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(x).to(dev)
+
+        nmax = max(w.tokens)
+        t0 = time.perf_counter()
+        h = to_dev(kd_synth.hidden(w, nmax))      # shorter token counts are row prefixes
+        wd = to_dev(kd_synth.student_head(w))
+        wt = to_dev(kd_synth.teacher_head(w))
+        log(f"{name}: inputs for N<={nmax} in {time.perf_counter() - t0:.1f}s")
+        for n in w.tokens:
+            for k in w.ks:
+                r = run_point(kd, torch, w, h, wd, wt, n, k, steps, warmup)
+                rows.append(r)
+                print(json.dumps(r), flush=True)
+                log(f"  N={n:7d} K={k:3d}: {r['tokens_per_s']:10.0f} tokens/s  {r['ms_per_step']:9.2f} ms  "
+                    f"MFMA {100 * r['mfma_util']:.1f}%  peak {r['peak_gb']:.2f} GB  cache {r['cache_build_ms']:.1f} ms")
+        del h, wd, wt
+        torch.cuda.empty_cache()
+    log("| workload | N | d | V | K | tokens/s | ms/step | MFMA util (8NVd, 2.5 PF) | peak GB | cache build ms |")
+    log("|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        log(f"| {r['workload']} | {r['n_tokens']:,} | {r['d']:,} | {r['vocab']:,} | {r['k']} | {r['tokens_per_s']:,.0f} | "
+            f"{r['ms_per_step']:.2f} | {100 * r['mfma_util']:.1f} % | {r['peak_gb']:.2f} | {r['cache_build_ms']:.1f} |")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +173,9 @@ def main() -> int:
     ap.add_argument("--no-cache-build-timing", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the single line: one JSON line per workload point (4K-256K tokens, "
+                         "every K) and a markdown table on stderr")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -120,6 +202,8 @@ def main() -> int:
         return 0
 
     kd.load_library()
+    if args.sweep:
+        return sweep(kd, torch, np, kd_synth, max(1, args.steps), args.warmup)
     dev = torch.device("cuda:0")
     w = kd_synth.WORKLOADS[args.workload]
     n = args.tokens or w.tokens[0]

@@ -94,51 +94,113 @@ __device__ __forceinline__ double block_sum_256(double v, double* sh) {
   return sh[0];
 }
 
+// Rows per block and threads per row of the per-row kernels (merge, scatter).
+constexpr int RB_ROWS = 16, RB_TPR = 16;
+
+// Combine two (max, sum exp) pairs of one row.
+__device__ __forceinline__ void lse_combine(float& M, float& S, float m2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (M == -INFINITY) {
+    M = m2;
+    S = s2;
+    return;
+  }
+  const float m = fmaxf(M, m2);
+  S = S * exp2f((M - m) * kLog2e) + s2 * exp2f((m2 - m) * kLog2e);
+  M = m;
+}
+
+// Reductions over the RB_TPR threads of one row: thread (r, q) is tid = r + RB_ROWS q,
+// so a wave holds 4 values of q per row (shuffles over lanes 16, 32 apart) and the
+// 4 waves meet in LDS.  Fixed order, so results are deterministic.
+__device__ __forceinline__ float row_sum(float v, float* sh) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  const int r = threadIdx.x & (RB_ROWS - 1), w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) < RB_ROWS) sh[w * RB_ROWS + r] = v;
+  __syncthreads();
+  return (sh[r] + sh[RB_ROWS + r]) + (sh[2 * RB_ROWS + r] + sh[3 * RB_ROWS + r]);
+}
+__device__ __forceinline__ float row_max(float v, float* sh) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  const int r = threadIdx.x & (RB_ROWS - 1), w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) < RB_ROWS) sh[w * RB_ROWS + r] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh[r], sh[RB_ROWS + r]), fmaxf(sh[2 * RB_ROWS + r], sh[3 * RB_ROWS + r]));
+}
+
 // Merge the per-tile (max, sum exp) partials of each row into lse, form the
 // teacher softmax over the K cached logits and the row's KL, and sum the block's
-// KL values (float64) for the deterministic loss reduction.
+// KL values (float64) for the deterministic loss reduction.  RB_ROWS rows per
+// block, RB_TPR threads per row striding the vocabulary tiles (partials of
+// consecutive rows are adjacent, so a wave's loads are coalesced over rows).
 template <typename VT>
 __global__ void __launch_bounds__(256) merge_kernel(const float2* __restrict__ partials, int64_t ld_part, int n_ty,
                                                     const int32_t* __restrict__ idx, const VT* __restrict__ val,
                                                     const float* __restrict__ zg, int nr, int kc, int vocab,
                                                     float inv_tau, float* __restrict__ lse_out,
                                                     float* __restrict__ kl_out, double* __restrict__ block_sums) {
-  __shared__ double sh[256];
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  double kl_d = 0.0;
-  if (t < nr) {
-    float M = -INFINITY, S = 0.f;
-    for (int y = 0; y < n_ty; ++y) {
+  __shared__ float sh[4 * RB_ROWS];
+  __shared__ float2 shp[4 * RB_ROWS];
+  __shared__ float klrow[RB_ROWS];
+  const int r = threadIdx.x & (RB_ROWS - 1), q = threadIdx.x / RB_ROWS;
+  const int t = blockIdx.x * RB_ROWS + r;
+  const bool valid = t < nr;
+  // (1) log-sum-exp over the vocabulary tiles
+  float M = -INFINITY, S = 0.f;
+  if (valid)
+    for (int y = q; y < n_ty; y += RB_TPR) {
       const float2 p = partials[(int64_t)y * ld_part + t];
-      if (p.x > M) {
-        S = S * exp2f((M - p.x) * kLog2e) + p.y;
-        M = p.x;
-      } else if (p.x != -INFINITY) {
-        S += p.y * exp2f((p.x - M) * kLog2e);
-      }
+      lse_combine(M, S, p.x, p.y);
     }
-    const float lse = M + logf(S);
-    const VT* vr = val + (int64_t)t * kc;
-    const int32_t* ir = idx + (int64_t)t * kc;
-    const float* zr = zg + (int64_t)t * kc;
-    float vmax = -INFINITY;
-    for (int k = 0; k < kc; ++k) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
-    float Z = 0.f;
-    for (int k = 0; k < kc; ++k) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
-    const float logZ = logf(Z);
-    float kl = 0.f;
-    for (int k = 0; k < kc; ++k) {
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) lse_combine(M, S, __shfl_xor(M, o), __shfl_xor(S, o));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) < RB_ROWS) shp[w * RB_ROWS + r] = make_float2(M, S);
+  __syncthreads();
+  M = shp[r].x;
+  S = shp[r].y;
+#pragma unroll
+  for (int i = 1; i < 4; ++i) lse_combine(M, S, shp[i * RB_ROWS + r].x, shp[i * RB_ROWS + r].y);
+  const float lse = M + logf(S);
+  // (2) teacher softmax over the K cached logits and the row's KL
+  const VT* vr = val + (int64_t)t * kc;
+  const int32_t* ir = idx + (int64_t)t * kc;
+  const float* zr = zg + (int64_t)t * kc;
+  float vmax = -INFINITY;
+  if (valid)
+    for (int k = q; k < kc; k += RB_TPR) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
+  vmax = row_max(vmax, sh);
+  float Z = 0.f;
+  if (valid)
+    for (int k = q; k < kc; k += RB_TPR) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
+  const float logZ = logf(row_sum(Z, sh));
+  float kl = 0.f;
+  if (valid)
+    for (int k = q; k < kc; k += RB_TPR) {
       const float lp = to_f32<VT>(vr[k]) * inv_tau - vmax - logZ;
       const float p = expf(lp);
       if ((unsigned)ir[k] >= (unsigned)vocab) kl = NAN;
       else kl += (p > 0.f ? p * lp : 0.f) - p * (zr[k] - lse);
     }
-    lse_out[t] = lse;
-    if (kl_out) kl_out[t] = kl;
-    kl_d = (double)kl;
+  kl = row_sum(kl, sh);
+  if (q == 0) {
+    klrow[r] = valid ? kl : 0.f;
+    if (valid) {
+      lse_out[t] = lse;
+      if (kl_out) kl_out[t] = kl;
+    }
   }
-  const double s = block_sum_256(kl_d, sh);
-  if (threadIdx.x == 0) block_sums[blockIdx.x] = s;
+  __syncthreads();
+  // (3) the block's KL sum over its rows, in row order (float64)
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (int i = 0; i < RB_ROWS; ++i) s += (double)klrow[i];
+    block_sums[blockIdx.x] = s;
+  }
 }
 
 // loss = (sum of block sums) / N, summed in a fixed order.
@@ -173,34 +235,60 @@ __global__ void __launch_bounds__(256) transpose_pad_kernel(const T* __restrict_
 
 // ---------------------------------------------------------------------------
 // Subtract the scaled teacher probabilities at the cached entries of each row
-// from dZ (and from dZ^T when that copy exists).  One thread owns one row, so repeated indices within a row
-// are applied in k order with no race.
+// from dZ (and from dZ^T when that copy exists).  RB_ROWS rows per block, RB_TPR
+// threads per row.  Entries are applied in batches of RB_TPR in k order: within a
+// batch, repeated indices are summed (in k order) by their first occurrence, and
+// a block barrier orders the batches, so every element is updated by one thread
+// at a time and repeated indices accumulate.
 template <typename T, typename VT>
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ idx, const VT* __restrict__ val,
                                                       int nr, int kc, int vocab, float inv_tau,
                                                       const float* __restrict__ grad, float inv_n,
                                                       T* __restrict__ dz, int64_t ldz, T* __restrict__ dzt,
                                                       int64_t ldzt) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= nr) return;
+  __shared__ float sh[4 * RB_ROWS];
+  __shared__ int bidx[RB_ROWS][RB_TPR];
+  __shared__ float bpe[RB_ROWS][RB_TPR];
+  const int r = threadIdx.x & (RB_ROWS - 1), q = threadIdx.x / RB_ROWS;
+  const int t = blockIdx.x * RB_ROWS + r;
+  const bool valid = t < nr;
   const float scale = (grad ? *grad : 1.0f) * inv_n;
   const VT* vr = val + (int64_t)t * kc;
   const int32_t* ir = idx + (int64_t)t * kc;
   float vmax = -INFINITY;
-  for (int k = 0; k < kc; ++k) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
+  if (valid)
+    for (int k = q; k < kc; k += RB_TPR) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
+  vmax = row_max(vmax, sh);
   float Z = 0.f;
-  for (int k = 0; k < kc; ++k) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
-  const float logZ = logf(Z);
-  for (int k = 0; k < kc; ++k) {
-    const int v = ir[k];
-    if ((unsigned)v >= (unsigned)vocab) continue;
-    const float pe = scale * expf(to_f32<VT>(vr[k]) * inv_tau - vmax - logZ);
-    T* a = dz + (int64_t)t * ldz + v;
-    *a = from_f32<T>(to_f32<T>(*a) - pe);
-    if (dzt) {
-      T* b = dzt + (int64_t)v * ldzt + t;
-      *b = from_f32<T>(to_f32<T>(*b) - pe);
+  if (valid)
+    for (int k = q; k < kc; k += RB_TPR) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
+  const float logZ = logf(row_sum(Z, sh));
+  for (int k0 = 0; k0 < kc; k0 += RB_TPR) {
+    const int k = k0 + q;
+    int v = -1;
+    float pe = 0.f;
+    if (valid && k < kc) {
+      v = ir[k];
+      if ((unsigned)v >= (unsigned)vocab) v = -1;
+      else pe = scale * expf(to_f32<VT>(vr[k]) * inv_tau - vmax - logZ);
     }
+    bidx[r][q] = v;
+    bpe[r][q] = pe;
+    __syncthreads();
+    bool first = v >= 0;
+    for (int j = 0; j < q && first; ++j) first = bidx[r][j] != v;
+    if (first) {
+      float sum = pe;
+      for (int j = q + 1; j < RB_TPR; ++j)
+        if (bidx[r][j] == v) sum += bpe[r][j];
+      T* a = dz + (int64_t)t * ldz + v;
+      *a = from_f32<T>(to_f32<T>(*a) - sum);
+      if (dzt) {
+        T* b = dzt + (int64_t)v * ldzt + t;
+        *b = from_f32<T>(to_f32<T>(*b) - sum);
+      }
+    }
+    __syncthreads();   // this batch's updates before the next batch's reads
   }
 }
 

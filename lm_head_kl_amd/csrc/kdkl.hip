@@ -116,7 +116,7 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     L->offsets = take(sizeof(int) * n_tx * (pl.n_ty + 1));
     L->zg = take(sizeof(float) * pl.Nc * pl.K);
     L->partials = take(sizeof(float2) * pl.n_ty * pl.Nc);
-    L->block_sums = take(sizeof(double) * (size_t)std::max<int64_t>(1, cdiv(pl.N, 256)));
+    L->block_sums = take(sizeof(double) * (size_t)std::max<int64_t>(1, cdiv(pl.N, RB_ROWS)));
     L->flags = take(sizeof(int) * 4);
   } else if (op == KD_OP_KL_BWD) {
     L->wt = take((size_t)(pl.esz * pl.d * pl.ld_v));
@@ -286,20 +286,20 @@ kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     g.partials = partials;
     g.ld_part = pl.Nc;
     KD_TRY((run_gemm<T, EPI_KL_FWD>("gemm_kl_fwd", g, (int64_t)8 * nr * pl.n_ty, st)));
-    const int nb = (int)cdiv(nr, 256);
+    const int nb = (int)cdiv(nr, RB_ROWS);
     const double mbytes = (double)nr * (8.0 * pl.n_ty + pl.K * (8.0 + vsz) + 8.0);
     KD_TRY(launch("merge", 0.0, mbytes, st, [&] {
       if (pl.vdt == KD_BF16)
         hipLaunchKernelGGL(merge_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty,
                            idx_c, (const bf16_t*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
-                           kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / 256);
+                           kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / RB_ROWS);
       else
         hipLaunchKernelGGL(merge_kernel<float>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty,
                            idx_c, (const float*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
-                           kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / 256);
+                           kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / RB_ROWS);
     }));
   }
-  const int nb_all = (int)cdiv(pl.N, 256);
+  const int nb_all = (int)cdiv(pl.N, RB_ROWS);
   KD_TRY(launch("loss", 0.0, 8.0 * nb_all, st, [&] {
     hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsums, nb_all, pl.N > 0 ? 1.0 / (double)pl.N : 0.0,
                        loss);
@@ -356,7 +356,7 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     g.inv_n = inv_n;
     KD_TRY((run_gemm<T, EPI_KL_DZ>("gemm_dz", g, (kKm ? 1 : 2) * es * nr * pl.V, st)));
     // subtract the teacher at the cached entries
-    const int nb = (int)cdiv(nr, 256);
+    const int nb = (int)cdiv(nr, RB_ROWS);
     KD_TRY(launch("scatter", 0.0, (double)nr * pl.K * (8.0 + (kKm ? 2.0 : 4.0) * es), st, [&] {
       if (pl.vdt == KD_BF16)
         hipLaunchKernelGGL((scatter_kernel<T, bf16_t>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,

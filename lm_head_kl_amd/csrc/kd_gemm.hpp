@@ -96,6 +96,10 @@ struct GemmArgs {
   int nx, ny, k;                  // valid rows of X and Y; contraction length
   int n_tx, n_ty, group;          // tile grid and tile-order grouping
   int krows_x, krows_y;           // K-major operands: rows of k that exist (rows past them read as 0)
+  // split-K (EPI_STORE_F32 only): n_tx * n_ty * splits workgroups; split s sums its
+  // share of the K stages into out + s * split_stride
+  int splits;
+  int64_t split_stride;
   // plain stores / dZ buffers
   void* out; int64_t ldo;         // P rows
   void* out2; int64_t ldo2;       // dZ^T rows (EPI_KL_DZ)
@@ -200,8 +204,9 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
   constexpr int KE = C::KB / ES;          // elements per stage
   constexpr int FX = C::FX, FY = C::FY, WX = C::WX, WY = C::WY, BXc = C::BX, BYc = C::BY;
 
+  const int split = (int)blockIdx.x / (a.n_tx * a.n_ty);
   int tx, ty;
-  tile_of(blockIdx.x, a.n_tx, a.n_ty, a.group, tx, ty);
+  tile_of((int)blockIdx.x - split * a.n_tx * a.n_ty, a.n_tx, a.n_ty, a.group, tx, ty);
   const int x0 = tx * BXc, y0 = ty * BYc;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -225,7 +230,10 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
     xs[f] = uint32_t((wx * WX + fr) * C::KB + ch * 16);
     ys[f] = uint32_t((BXc + wy * WY + fr) * C::KB + ch * 16);
   }
-  const int nk = (a.k + KE - 1) / KE;
+  const int nk_all = (a.k + KE - 1) / KE;
+  const int k_per = (nk_all + a.splits - 1) / a.splits;
+  const int st0 = split * k_per;                          // this workgroup's first stage
+  const int nk = max(0, min(k_per, nk_all - st0));
   {
     // ---- LDS-DMA pipeline.  Stage kt lives in LDS buffer kt % 2.
     constexpr int DPW = C::DMA_PER_WAVE;
@@ -271,7 +279,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
                         : uint32_t((m * RPB + lrow) * ldb + lch * 16);
     }
     auto issue = [&](int stage, int buf) {
-      const int k0 = stage * KE;
+      const int k0 = (st0 + stage) * KE;
       const uint32_t ldsb = lds_base + uint32_t(buf * C::STAGE_BYTES + wave * DPW * 1024);
       if (wave_km) {
         // one descriptor per stage from k-row k0, column 0 of the operand's rows: rows
@@ -332,7 +340,8 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
       mma(h0x, h0y);                     // first half of stage kt
       wait_vmcnt<0>();                   // own loads of stage kt + 1 have landed
       __syncthreads();                   // everyone's; every read of stage kt is done
-      issue(kt + 2, cur);                // stage kt + 2 into stage kt's buffer (zeros past the end)
+      issue(kt + 2, cur);                // stage kt + 2 into stage kt's buffer (past K: zeros;
+                                         // past this split's stages: loaded, never read)
       rdfrag(h0x, h0y, cur ^ 1, 0);      // first half of stage kt + 1
       mma(h1x, h1y);                     // second half of stage kt
     }
@@ -350,7 +359,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
     for (int i = 0; i < FX; ++i) {
       const int n = nrow0 + i * 16;
       if (n >= a.out_rows) continue;
-      OT* orow = (OT*)a.out + (int64_t)n * a.ldo;
+      OT* orow = (OT*)a.out + split * a.split_stride + (int64_t)n * a.ldo;
 #pragma unroll
       for (int j = 0; j < FY; ++j) {
         const int m = mcol + j * 16;

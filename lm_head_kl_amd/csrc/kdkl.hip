@@ -26,6 +26,8 @@ constexpr int kMaxKTopk = 4096;          // selection candidates are held in LDS
 constexpr int64_t kDefaultChunkKL = 16384;
 constexpr int64_t kDefaultChunkTopk = 8192;
 constexpr int kGroup = 4;   // X tiles walked per Y tile (measured best for all four GEMM shapes)
+constexpr int kMinTiles = 256;   // workgroups that fill MI355X's compute units (one 256 x 256 tile each)
+constexpr int kMaxSplits = 16;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -54,7 +56,7 @@ struct Plan {
 // Workspace regions, each 256-byte aligned, in bytes from the workspace start.
 struct Layout {
   size_t entries, offsets, zg, partials, block_sums, flags;       // forward
-  size_t wt, ht, dz, dzt;                                         // backward
+  size_t wt, ht, dz, dzt, dhp;                                    // backward
   size_t s, bmax, wmax, overflow, tops, todo;                     // cache build
   size_t total;
 };
@@ -102,6 +104,18 @@ kd_status validate(kd_op op, const kd_problem* p, Plan* pl) {
   return KD_OK;
 }
 
+// Split-K factor of the dH product for a chunk of nr tokens: when its output tiles
+// cannot fill the device's compute units, each tile's V range is cut into parts
+// (at least 8 K stages each) summed afterwards in a fixed order.
+int dh_splits(const Plan& pl, int64_t nr) {
+  const int64_t tiles = cdiv(nr, BX) * cdiv(pl.d, BY);
+  if (nr <= 0 || tiles >= kMinTiles) return 1;
+  const int64_t stages = cdiv(pl.V_pad, MainCfg::KB / pl.esz);
+  int64_t s = std::min<int64_t>(kMaxSplits, kMinTiles / tiles);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
+  return (int)std::max<int64_t>(1, s);
+}
+
 size_t layout(kd_op op, const Plan& pl, Layout* L) {
   size_t cur = 0;
   auto take = [&](size_t bytes) {
@@ -125,6 +139,13 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     // bf16 reads dZ K-major in the dW product; float32 (no transposing LDS read)
     // keeps a transposed copy
     if (pl.xdt == KD_F32) L->dzt = take((size_t)(pl.esz * pl.V_pad * pl.ld_t));
+    // split-K partials of dH: the full chunks and the last, shorter one
+    const int64_t last = pl.N % pl.Nc;
+    const int64_t full = pl.N >= pl.Nc ? pl.Nc : 0;
+    int64_t part = 0;
+    for (int64_t nr : {full, last})
+      if (nr > 0 && dh_splits(pl, nr) > 1) part = std::max<int64_t>(part, dh_splits(pl, nr) * nr * pl.d);
+    if (part) L->dhp = take((size_t)(4 * part));
   } else {
     L->s = take(sizeof(float) * (size_t)(pl.Nc * pl.ld_v));
     L->bmax = take(sizeof(double) * 1024);
@@ -235,13 +256,14 @@ GemmArgs gemm_args(const void* X, int64_t ldx, int nx, const void* Y, int64_t ld
   g.n_tx = (int)cdiv(nx, BX);
   g.n_ty = (int)cdiv(ny, BY);
   g.group = kGroup;
+  g.splits = 1;
   return g;
 }
 
 template <typename T, int EPI, int XKM = 0, int YKM = 0>
 kd_status run_gemm(const char* kind, const GemmArgs& g, int64_t out_bytes, hipStream_t st) {
   if (g.nx <= 0 || g.ny <= 0) return KD_OK;
-  const unsigned blocks = (unsigned)(g.n_tx * g.n_ty);
+  const unsigned blocks = (unsigned)(g.n_tx * g.n_ty * g.splits);
   const double flops = 2.0 * g.nx * (double)g.ny * g.k;
   const double bytes = (double)sizeof(T) * ((double)g.nx + g.ny) * g.k + (double)out_bytes;
   return launch(kind, flops, bytes, st, [&] {
@@ -372,7 +394,25 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     gh.out_rows = nr;
     gh.out_cols = (int)pl.d;
     gh.ldo = pl.d;
-    if (pl.dhdt == KD_F32) {
+    const int S = dh_splits(pl, nr);
+    if (S > 1) {
+      // too few output tiles to fill the device: S partial sums over V, then their sum
+      float* part = (float*)(ws + L.dhp);
+      gh.out = part;
+      gh.splits = S;
+      gh.split_stride = (int64_t)nr * pl.d;
+      KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_dh", gh, 4 * S * nr * pl.d, st)));
+      const int64_t n4 = (int64_t)nr * pl.d / 4;
+      const unsigned nb = (unsigned)std::min<int64_t>(4096, cdiv(n4, 256));
+      KD_TRY(launch("dh_split_sum", 0.0, 4.0 * (S + 1) * nr * pl.d, st, [&] {
+        if (pl.dhdt == KD_F32)
+          hipLaunchKernelGGL(split_reduce_kernel<float>, dim3(nb), dim3(256), 0, st, part, S, gh.split_stride, n4,
+                             (float*)dh + r0 * pl.d);
+        else
+          hipLaunchKernelGGL(split_reduce_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, part, S, gh.split_stride, n4,
+                             (bf16_t*)dh + r0 * pl.d);
+      }));
+    } else if (pl.dhdt == KD_F32) {
       gh.out = (float*)dh + r0 * pl.d;
       KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_dh", gh, 4 * nr * pl.d, st)));
     } else {

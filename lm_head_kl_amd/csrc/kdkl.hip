@@ -28,6 +28,12 @@ constexpr int64_t kDefaultChunkTopk = 8192;
 constexpr int kGroup = 4;   // X tiles walked per Y tile (measured best for all four GEMM shapes)
 constexpr int kMinTiles = 256;   // workgroups that fill MI355X's compute units (one 256 x 256 tile each)
 constexpr int kMaxSplits = 16;
+// Up to this many tokens the backward reads W K-major in the dH product instead of
+// making W^T.  Both costs scale with V d: measured at V=128,256, d=4,096 the copy
+// takes 0.83 ms and the transposing read adds ~0.09 ms per 1,024 tokens to dH, so
+// the copy only pays from ~9K tokens (4K tokens: step 14.97 -> 14.28 ms; 16K: 53.7
+// -> 56.1 ms, hence the bound).
+constexpr int64_t kWkmMaxTokens = 4096;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -133,7 +139,7 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     L->block_sums = take(sizeof(double) * (size_t)std::max<int64_t>(1, cdiv(pl.N, RB_ROWS)));
     L->flags = take(sizeof(int) * 4);
   } else if (op == KD_OP_KL_BWD) {
-    L->wt = take((size_t)(pl.esz * pl.d * pl.ld_v));
+    if (!(pl.xdt == KD_BF16 && pl.N <= kWkmMaxTokens)) L->wt = take((size_t)(pl.esz * pl.d * pl.ld_v));
     L->ht = take((size_t)(pl.esz * pl.d * pl.ld_t));
     L->dz = take((size_t)(pl.esz * pl.Nc * pl.ld_v));
     // bf16 reads dZ K-major in the dW product; float32 (no transposing LDS read)
@@ -335,6 +341,14 @@ kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
   return KD_OK;
 }
 
+template <typename T, int EPI>
+kd_status run_dh(const GemmArgs& g, bool w_kmajor, int64_t out_bytes, hipStream_t st) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (w_kmajor) return run_gemm<T, EPI, 0, 1>("gemm_dh", g, out_bytes, st);
+  }
+  return run_gemm<T, EPI>("gemm_dh", g, out_bytes, st);
+}
+
 template <typename T>
 kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
                    const void* val, const float* lse, const float* grad, void* dh, float* dw, char* ws,
@@ -351,11 +365,14 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
   const float inv_n = 1.0f / (float)pl.N;
   const float inv_tau = 1.0f / pl.tau;
   const int64_t es = (int64_t)sizeof(T);
-  // W^T [d][V_pad], zero past V
-  KD_TRY(launch("transpose_w", 0.0, 2.0 * es * pl.V * pl.d, st, [&] {
-    hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(pl.V_pad, 64), (unsigned)cdiv(pl.d, 64)),
-                       dim3(256), 0, st, (const T*)w, pl.d, (int)pl.V, (int)pl.d, wt, pl.ld_v, (int)pl.V_pad);
-  }));
+  const bool w_km = kKm && pl.N <= kWkmMaxTokens;
+  if (!w_km) {
+    // W^T [d][V_pad], zero past V
+    KD_TRY(launch("transpose_w", 0.0, 2.0 * es * pl.V * pl.d, st, [&] {
+      hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(pl.V_pad, 64), (unsigned)cdiv(pl.d, 64)),
+                         dim3(256), 0, st, (const T*)w, pl.d, (int)pl.V, (int)pl.d, wt, pl.ld_v, (int)pl.V_pad);
+    }));
+  }
   for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
     const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
     const int nr64 = (int)round_up(nr, 64);
@@ -389,8 +406,10 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
                            (const float*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.ld_v,
                            dzt, pl.ld_t);
     }));
-    // dH = dZ W  (P[t][j] = sum_v dZ[t][v] W^T[j][v])
-    GemmArgs gh = gemm_args(dz, pl.ld_v, nr, wt, pl.ld_v, (int)pl.d, (int)pl.V_pad);
+    // dH = dZ W  (P[t][j] = sum_v dZ[t][v] W^T[j][v], or W read K-major)
+    GemmArgs gh = w_km ? gemm_args(dz, pl.ld_v, nr, w, pl.d, (int)pl.d, (int)pl.V_pad)
+                       : gemm_args(dz, pl.ld_v, nr, wt, pl.ld_v, (int)pl.d, (int)pl.V_pad);
+    gh.krows_y = (int)pl.V;
     gh.out_rows = nr;
     gh.out_cols = (int)pl.d;
     gh.ldo = pl.d;
@@ -401,7 +420,7 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
       gh.out = part;
       gh.splits = S;
       gh.split_stride = (int64_t)nr * pl.d;
-      KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_dh", gh, 4 * S * nr * pl.d, st)));
+      KD_TRY((run_dh<T, EPI_STORE_F32>(gh, w_km, 4 * S * nr * pl.d, st)));
       const int64_t n4 = (int64_t)nr * pl.d / 4;
       const unsigned nb = (unsigned)std::min<int64_t>(4096, cdiv(n4, 256));
       KD_TRY(launch("dh_split_sum", 0.0, 4.0 * (S + 1) * nr * pl.d, st, [&] {
@@ -414,10 +433,10 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
       }));
     } else if (pl.dhdt == KD_F32) {
       gh.out = (float*)dh + r0 * pl.d;
-      KD_TRY((run_gemm<T, EPI_STORE_F32>("gemm_dh", gh, 4 * nr * pl.d, st)));
+      KD_TRY((run_dh<T, EPI_STORE_F32>(gh, w_km, 4 * nr * pl.d, st)));
     } else {
       gh.out = (bf16_t*)dh + r0 * pl.d;
-      KD_TRY((run_gemm<T, EPI_STORE_BF16>("gemm_dh", gh, 2 * nr * pl.d, st)));
+      KD_TRY((run_dh<T, EPI_STORE_BF16>(gh, w_km, 2 * nr * pl.d, st)));
     }
     // dW (+)= dZ^T H  (P[v][j] = sum_t dZ[t][v] H^T[j][t]; bf16 reads X = dZ K-major)
     GemmArgs gw = kKm ? gemm_args(dz, pl.ld_v, (int)pl.V, ht, pl.ld_t, (int)pl.d, nr64)

@@ -92,7 +92,7 @@ def test_workspace_size_null_and_bad_op(lib):
 def test_workspace_is_chunk_sized_not_token_sized(lib):
     """Peak-memory linearity: the big workspace terms depend on the chunk, not N."""
     sizes = {}
-    for n in (16384, 65536, 262144):
+    for n in (16384, 65536, 262144):    # at or above one chunk (below 4K tokens the backward skips W^T)
         for op in (kd.KD_OP_KL_FWD, kd.KD_OP_KL_BWD):
             st, b = _ws(lib, op, _P(n=n, d=4096, v=128256, k=100, chunk_tokens=16384))
             assert st == 0

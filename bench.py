@@ -255,7 +255,9 @@ def main() -> int:
     kd.profile_begin()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    out = None
     for i in range(args.steps):
+        out = None          # a training loop has consumed the previous step's gradients
         out = step()
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start

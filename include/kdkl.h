@@ -58,9 +58,9 @@
  *     kernels (no out-of-bounds access); it makes that row's KL NaN, and when the
  *     environment variable KD_CHECK=1 is set the forward call synchronises the
  *     stream and returns KD_ERR_IDX_OUT_OF_RANGE.
- *   - Results are bitwise reproducible for a given shape, chunk size and device
- *     (no floating-point atomics), except the gradient of a row whose cached
- *     indices repeat.
+ *   - Results are bitwise reproducible for a given shape, chunk size and device:
+ *     there are no floating-point atomics, every reduction has a fixed order, and
+ *     repeated indices in a row are applied in k order.
  */
 #ifndef KDKL_H
 #define KDKL_H

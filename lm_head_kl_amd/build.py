@@ -48,7 +48,29 @@ def build(verbose: bool = False) -> str:
     if verbose and out.strip():
         print(out)
     os.replace(tmp, OUT)
+    build_c_client(verbose)
     return OUT
+
+
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi", "kd_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c_abi", "kd_client")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Compile the plain-C client of the ABI (tests/c_abi/kd_client) against the
+    library just built and the HIP runtime's C API; no HIP device code."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+           "-I", os.path.join(ROOT, "include"), C_CLIENT_SRC, "-o", C_CLIENT + ".tmp", "-L", PKG, "-lkdkl",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../lm_head_kl_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed ({r.returncode}):\n{r.stdout}")
+    os.replace(C_CLIENT + ".tmp", C_CLIENT)
+    return C_CLIENT
 
 
 if __name__ == "__main__":

@@ -1,0 +1,121 @@
+/*
+ * Plain-C client of the kdkl C ABI (include/kdkl.h), linked against libkdkl.so and
+ * the HIP runtime's C API only.  It reads a problem file, builds the teacher's
+ * top-K cache, runs the forward and the backward, and writes the results:
+ *
+ *   kd_client IN OUT
+ *   IN : int64 N, d, V; int32 K; float tau; then H [N*d], W [V*d], W_T [V*d] as bf16
+ *        bits (uint16), teacher hidden states = H
+ *   OUT: int32 status; then idx [N*K] int32, val [N*K] bf16 bits, loss float,
+ *        lse [N] float, dH [N*d] float, dW [V*d] float
+ *
+ * Exit status 0 on success; on a library error the kd_status is printed with
+ * kd_status_string() and the exit status is 1.
+ */
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "kdkl.h"
+
+#define HIP_OK(x)                                                             \
+  do {                                                                        \
+    if ((x) != hipSuccess) {                                                  \
+      fprintf(stderr, "kd_client: HIP call failed: %s\n", #x);                \
+      return 2;                                                               \
+    }                                                                         \
+  } while (0)
+
+#define KD_OK_OR_FAIL(x)                                                      \
+  do {                                                                        \
+    kd_status s_ = (x);                                                       \
+    if (s_ != KD_OK) {                                                        \
+      fprintf(stderr, "kd_client: %s -> %s\n", #x, kd_status_string(s_));     \
+      return 1;                                                               \
+    }                                                                         \
+  } while (0)
+
+static int read_all(FILE* f, void* p, size_t n) { return fread(p, 1, n, f) == n; }
+static int write_all(FILE* f, const void* p, size_t n) { return fwrite(p, 1, n, f) == n; }
+
+int main(int argc, char** argv) {
+  if (argc != 3) {
+    fprintf(stderr, "usage: kd_client IN OUT\n");
+    return 2;
+  }
+  FILE* fi = fopen(argv[1], "rb");
+  if (!fi) return 2;
+  int64_t dims[3];
+  int32_t K;
+  float tau;
+  if (!read_all(fi, dims, sizeof dims) || !read_all(fi, &K, sizeof K) || !read_all(fi, &tau, sizeof tau)) return 2;
+  const int64_t N = dims[0], d = dims[1], V = dims[2];
+  const size_t nh = (size_t)(N * d), nw = (size_t)(V * d), nk = (size_t)(N * K);
+  uint16_t* h = malloc(2 * nh);
+  uint16_t* w = malloc(2 * nw);
+  uint16_t* wt = malloc(2 * nw);
+  if (!h || !w || !wt) return 2;
+  if (!read_all(fi, h, 2 * nh) || !read_all(fi, w, 2 * nw) || !read_all(fi, wt, 2 * nw)) return 2;
+  fclose(fi);
+
+  kd_problem p = {N, d, V, K, tau, KD_BF16, KD_BF16, KD_F32, 0};
+  size_t ws_bytes = 0, b = 0;
+  KD_OK_OR_FAIL(kd_workspace_size(KD_OP_TOPK_BUILD, &p, &b));
+  if (b > ws_bytes) ws_bytes = b;
+  KD_OK_OR_FAIL(kd_workspace_size(KD_OP_KL_FWD, &p, &b));
+  if (b > ws_bytes) ws_bytes = b;
+  KD_OK_OR_FAIL(kd_workspace_size(KD_OP_KL_BWD, &p, &b));
+  if (b > ws_bytes) ws_bytes = b;
+
+  void *dh_in, *dw_in, *dwt_in, *didx, *dval, *dloss, *dlse, *ddh, *ddw, *dws;
+  HIP_OK(hipMalloc(&dh_in, 2 * nh));
+  HIP_OK(hipMalloc(&dw_in, 2 * nw));
+  HIP_OK(hipMalloc(&dwt_in, 2 * nw));
+  HIP_OK(hipMalloc(&didx, 4 * nk + 16));
+  HIP_OK(hipMalloc(&dval, 2 * nk + 16));
+  HIP_OK(hipMalloc(&dloss, 16));
+  HIP_OK(hipMalloc(&dlse, 4 * (size_t)N + 16));
+  HIP_OK(hipMalloc(&ddh, 4 * nh + 16));
+  HIP_OK(hipMalloc(&ddw, 4 * nw));
+  HIP_OK(hipMalloc(&dws, ws_bytes ? ws_bytes : 16));
+  HIP_OK(hipMemcpy(dh_in, h, 2 * nh, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dw_in, w, 2 * nw, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dwt_in, wt, 2 * nw, hipMemcpyHostToDevice));
+
+  hipStream_t st;
+  HIP_OK(hipStreamCreate(&st));
+  KD_OK_OR_FAIL(kd_topk_cache_build(&p, dh_in, dwt_in, (int32_t*)didx, dval, dws, ws_bytes, st));
+  KD_OK_OR_FAIL(kd_chunked_kl_fwd(&p, dh_in, dw_in, (const int32_t*)didx, dval, (float*)dloss, (float*)dlse,
+                                  NULL, dws, ws_bytes, st));
+  KD_OK_OR_FAIL(kd_chunked_kl_bwd(&p, dh_in, dw_in, (const int32_t*)didx, dval, (const float*)dlse, NULL, ddh,
+                                  (float*)ddw, dws, ws_bytes, st));
+  HIP_OK(hipStreamSynchronize(st));
+
+  int32_t* idx = malloc(4 * nk + 4);
+  uint16_t* val = malloc(2 * nk + 2);
+  float* lse = malloc(4 * (size_t)N + 4);
+  float* dhh = malloc(4 * nh + 4);
+  float* dwh = malloc(4 * nw);
+  float loss = 0.f;
+  if (!idx || !val || !lse || !dhh || !dwh) return 2;
+  HIP_OK(hipMemcpy(idx, didx, 4 * nk, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(val, dval, 2 * nk, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&loss, dloss, 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(lse, dlse, 4 * (size_t)N, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(dhh, ddh, 4 * nh, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(dwh, ddw, 4 * nw, hipMemcpyDeviceToHost));
+
+  FILE* fo = fopen(argv[2], "wb");
+  if (!fo) return 2;
+  const int32_t ok = 0;
+  if (!write_all(fo, &ok, 4) || !write_all(fo, idx, 4 * nk) || !write_all(fo, val, 2 * nk) ||
+      !write_all(fo, &loss, 4) || !write_all(fo, lse, 4 * (size_t)N) || !write_all(fo, dhh, 4 * nh) ||
+      !write_all(fo, dwh, 4 * nw))
+    return 2;
+  fclose(fo);
+  printf("kd_client: N=%lld d=%lld V=%lld K=%d loss=%.6f (kd_version %d)\n", (long long)N, (long long)d,
+         (long long)V, K, loss, kd_version());
+  HIP_OK(hipStreamDestroy(st));
+  return 0;
+}

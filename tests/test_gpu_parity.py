@@ -208,12 +208,19 @@ def test_out_of_range_index_gives_nan_row_not_a_fault():
     assert np.isnan(loss.item())
 
 
-def test_repeated_indices_scatter_add():
-    n, d, v, k = 260, 64, 300, 6
+@pytest.mark.parametrize("k,span", [(6, None), (40, 20)])
+def test_repeated_indices_scatter_add(k, span):
+    """Repeated indices in a row are separate entries: the gradient scatter-adds them.
+    (40, 20): every row draws 40 entries from 20 vocabulary ids, so repeats fall both
+    inside one batch of the scatter and across batches; the result is also checked
+    to be bitwise reproducible."""
+    n, d, v = 260, 64, 300
     p = kd_synth.small_problem(n, d, v, seed=8)
     H = kd_synth.to_float64(p["H"], "bf16")
     W = kd_synth.to_float64(p["W"], "bf16")
     idx, valb = kd_synth.random_cache(n, v, k, seed=2, distinct=False)
+    if span is not None:
+        idx = (idx % span).astype(np.int32)
     val = kd_synth.to_float64(valb, "bf16")
     ref_dH, ref_dW = oracle.kl_backward(H, W, idx, val, 1.0)
     ref_loss, _, _ = oracle.kl_forward(H, W, idx, val, 1.0)
@@ -221,10 +228,12 @@ def test_repeated_indices_scatter_add():
     ti, tv = torch.from_numpy(idx).to(device()), to_dev(valb, "bf16")
     loss, lse, _ = kd.kd_chunked_kl_fwd(h, w, ti, tv, 1.0)
     dh, dw = kd.kd_chunked_kl_bwd(h, w, ti, tv, 1.0, lse)
+    dh2, dw2 = kd.kd_chunked_kl_bwd(h, w, ti, tv, 1.0, lse)
     torch.cuda.synchronize()
     assert abs(loss.item() - ref_loss) <= LOSS_RTOL * abs(ref_loss)
     assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL
     assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+    assert torch.equal(dh, dh2) and torch.equal(dw, dw2)
 
 
 def test_autograd_function():

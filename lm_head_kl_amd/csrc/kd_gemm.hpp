@@ -328,6 +328,23 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
 #pragma unroll
         for (int j = 0; j < FY; ++j) Mma<T>::run(acc[i][j], by[j], bx[i]);
     };
+    // With a K-major operand (twice the LDS reads: two transposing reads per fragment)
+    // the next half's reads are spread over this half's MFMAs, one read per two MFMAs
+    // (measured: dW 2.7 % faster).  Row-major operands keep the compiler's schedule,
+    // which measured 3 % faster than this interleave for them.
+    auto interleave = [&]() {
+      if constexpr (XKM || YKM) {
+        constexpr int NREAD = (XKM ? 2 : 1) * FX + (YKM ? 2 : 1) * FY;
+        constexpr int NMMA = FX * FY;
+        constexpr int PER = NMMA / NREAD > 0 ? NMMA / NREAD : 1;
+#pragma unroll
+        for (int r = 0; r < NREAD; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0); // then PER MFMAs
+        }
+        if constexpr (NMMA > PER * NREAD) __builtin_amdgcn_sched_group_barrier(0x008, NMMA - PER * NREAD, 0);
+      }
+    };
     issue(0, 0);
     wait_vmcnt<0>();
     __syncthreads();
@@ -338,12 +355,14 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
       const int cur = kt & 1;
       rdfrag(h1x, h1y, cur, 1);          // second half of stage kt
       mma(h0x, h0y);                     // first half of stage kt
+      interleave();
       wait_vmcnt<0>();                   // own loads of stage kt + 1 have landed
       __syncthreads();                   // everyone's; every read of stage kt is done
       issue(kt + 2, cur);                // stage kt + 2 into stage kt's buffer (past K: zeros;
                                          // past this split's stages: loaded, never read)
       rdfrag(h0x, h0y, cur ^ 1, 0);      // first half of stage kt + 1
       mma(h1x, h1y);                     // second half of stage kt
+      interleave();
     }
     wait_vmcnt<0>();
     __syncthreads();

@@ -491,8 +491,9 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
 //  1. Those 2 n_ty values are distinct elements of the row, so their K-th largest
 //     t is <= the row's K-th largest float32 logit (bitwise search over the
 //     order-preserving keys, 32 block counts).
-//  2. One pass over the row keeps every logit >= t - 2 eps (eps as in the general
-//     path): the exact top-K are all among them.
+//  2. One pass over the row's tiles whose largest logit reaches t - 2 eps keeps
+//     every logit >= t - 2 eps (eps as in the general path): the exact top-K are
+//     all among them.
 //  3. float64 re-scoring, ranking by (score desc, index asc), first K written.
 // A row this path cannot take (2 n_ty < K, more tile values than TOPS_CAP, more
 // candidates than FAST_CAP) is flagged in rows_todo for the general kernel.
@@ -548,13 +549,18 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_fast_kernel(
   hn = sqrt(block_sum_256(hn, shd));
   const double eps = 2.0 * (double)d * 0x1p-23 * hn * (*wmax);
   const float thr = __double2float_rd((double)key_float(t) - 2.0 * eps);
-  // 2. candidates (V is a multiple of 4 or the tail is handled by the index test)
-  const int nq = (V + 3) / 4;
-  for (int q = tid; q < nq; q += SEL_THREADS) {
-    const f32x4 x = *(const f32x4*)(s + 4 * q);
+  // 2. candidates.  A vocabulary tile whose largest logit is below the threshold
+  // holds none, so only the other tiles are read (one wave per 256-column tile,
+  // 16 bytes per lane; the index test covers the vocabulary tail).
+  const uint32_t thr_key = float_key(thr);
+  for (int q = wave; q < n_ty; q += SEL_THREADS / 64) {
+    if (keys[2 * q] < thr_key) continue;
+    const int v0 = 256 * q + 4 * lane;
+    if (v0 >= V) continue;
+    const f32x4 x = *(const f32x4*)(s + v0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int v = 4 * q + e;
+      const int v = v0 + e;
       if (v < V && x[e] >= thr) {
         const int pos = atomicAdd(&ncand, 1);
         if (pos < FAST_CAP) cidx[pos] = v;

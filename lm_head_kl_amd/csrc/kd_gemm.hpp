@@ -16,9 +16,12 @@
 //    (out-of-range buffer offsets), so tails need no branches;
 //  * LDS holds 2 stages of 128 bytes of K per row (64 bf16 / 32 fp32); the load of
 //    stage kt + 2 is issued right after the barrier that frees stage kt's buffer;
-//  * each stage is two 64-byte MFMA fragments; the fragments of the next half are
-//    always read from LDS while the MFMAs of the current half run (one barrier per
-//    stage, placed between the halves);
+//  * each stage is two 64-byte MFMA fragments; in source order the fragments of the
+//    next half are read from LDS before the MFMAs of the current half (one barrier
+//    per stage, placed between the halves).  For row-major operands the compiler
+//    then moves each read next to its first use (the two waves of a SIMD cover each
+//    other's waits); with a K-major operand scheduling-group barriers keep the reads
+//    spread over the MFMAs;
 //  * the 16-byte chunks of each LDS row are XOR-swizzled by row % 8, which makes the
 //    fragment reads (ds_read_b128, lane = row l % 16, chunk l / 16) free of bank
 //    conflicts on gfx950 (measured: 4 LDS cycles per read, 256 B/clk);

@@ -83,6 +83,7 @@ def test_topk_cache_bit_exact(shape):
     (64, 64, 65536, 500),   # one-pass path, ~1,250 candidates per row (large ranking)
     (64, 64, 65536, 510),   # bound near the bottom of the tile values: ~1,700 candidates,
                             # most rows exceed the one-pass buffer and go to the radix path
+    (96, 64, 3001, 8),      # one-pass path, vocabulary not a multiple of 4 (185-column last tile)
 ], ids=lambda c: "x".join(map(str, c)))
 def test_topk_selection_paths(case):
     """The one-pass selection and its hand-over to the radix kernel in one call;
@@ -119,6 +120,25 @@ def test_large_logit_scale(scale):
     np.testing.assert_allclose(to_f64(rows), ref_rows, rtol=5e-3, atol=5e-3)
     assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL
     assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+
+
+@pytest.mark.parametrize("dh_dtype", [torch.float32, torch.bfloat16])
+def test_split_k_dh(dh_dtype):
+    """Few tokens and a narrow head: dH has fewer output tiles than compute units, so
+    its V range is split and the float32 partials are summed (then rounded to bf16)."""
+    n, d, v, k, tau = 200, 256, 5000, 12, 1.0
+    p, H, W, WT, idx, val = _problem(n, d, v, k, "bf16", seed=13)
+    ref_dH, ref_dW = oracle.kl_backward(H, W, idx, _val64(val, "bf16"), tau)
+    h, w = to_dev(p["H"], "bf16"), to_dev(p["W"], "bf16")
+    ti, tv = torch.from_numpy(idx).to(device()), to_dev(val, "bf16")
+    _, lse, _ = kd.kd_chunked_kl_fwd(h, w, ti, tv, tau)
+    dh, dw = kd.kd_chunked_kl_bwd(h, w, ti, tv, tau, lse, dh_dtype=dh_dtype)
+    dh2, _ = kd.kd_chunked_kl_bwd(h, w, ti, tv, tau, lse, dh_dtype=dh_dtype)
+    torch.cuda.synchronize()
+    assert dh.dtype == dh_dtype
+    assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL
+    assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+    assert torch.equal(dh, dh2)
 
 
 def _tiny_config():

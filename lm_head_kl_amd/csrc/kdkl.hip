@@ -103,7 +103,6 @@ kd_status validate(kd_op op, const kd_problem* p, Plan* pl) {
   pl->ld_v = pad_ld(pl->V_pad, op == KD_OP_TOPK_BUILD ? 4 : pl->esz);
   pl->ld_t = pad_ld(pl->Nc, pl->esz);
   pl->n_ty = (int)cdiv(pl->V, BY);
-  // 32-bit offsets inside one 256-row tile of every GEMM operand
   // 32-bit byte offsets inside one 256-row tile of every GEMM operand
   if (!mul_ok(BX * 4, std::max<int64_t>(std::max<int64_t>(pl->ld_v, pl->ld_t), pl->d), INT32_MAX))
     return KD_ERR_BAD_SHAPE;

@@ -159,6 +159,54 @@ def sweep(kd, torch, np, kd_synth, steps, warmup):
     return 0
 
 
+def cache_io(kd, torch, idx, val, vocab, shards=4, batch=16384, prefetch=3):
+    """Write the built cache to shards in a temporary directory and stream it back
+    to the device with the loader (the files were just written, so this measures the
+    page cache and the upload path, not a disk).  Checks the streamed cache is the
+    original, bit for bit."""
+    import shutil
+    import tempfile
+    ih, vh = idx.cpu(), val.cpu()
+    n = ih.shape[0]
+    d = tempfile.mkdtemp(prefix="kdcache_")
+    try:
+        paths = [os.path.join(d, f"part{i:03d}.kdc") for i in range(shards)]
+        cuts = [n * i // shards for i in range(shards + 1)]
+        t0 = time.perf_counter()
+        for i, p in enumerate(paths):
+            kd.kd_cache_write(p, ih[cuts[i]:cuts[i + 1]].contiguous(), vh[cuts[i]:cuts[i + 1]].contiguous(), vocab)
+        t_write = time.perf_counter() - t0
+        nbytes = sum(os.path.getsize(p) for p in paths)
+        bits = kd.kd_cache_info_read(paths[0])["idx_bits"]
+        li, lv = torch.empty_like(idx), torch.empty_like(val)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h = kd.kd_cache_loader_open(paths, batch, prefetch)
+        try:
+            row = 0
+            while True:
+                r = kd.kd_cache_loader_next(h, li[row:row + batch], lv[row:row + batch])
+                if r == 0:
+                    break
+                row += r
+        finally:
+            kd.kd_cache_loader_close(h)
+        torch.cuda.synchronize()
+        t_load = time.perf_counter() - t0
+        exact = bool(torch.equal(li, idx)) and bool(torch.equal(lv.view(torch.int16 if lv.dtype == torch.bfloat16
+                                                                         else torch.int32),
+                                                                val.view(torch.int16 if val.dtype == torch.bfloat16
+                                                                         else torch.int32)))
+        if not exact or row != n:
+            raise RuntimeError("cache streamed back through the loader differs from the cache written")
+        return {"bytes": nbytes, "shards": shards, "idx_bits": bits, "batch_tokens": batch,
+                "write_gbs": nbytes / t_write / 1e9, "load_gbs": nbytes / t_load / 1e9,
+                "load_tokens_per_s": n / t_load, "exact": exact,
+                "note": "files in the page cache; host->device through pinned buffers"}
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +219,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-build-timing", action="store_true")
+    ap.add_argument("--no-cache-io", action="store_true",
+                    help="skip writing the cache to shards and streaming it back with the loader")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration) and exit")
     ap.add_argument("--sweep", action="store_true",
@@ -294,6 +344,12 @@ def main() -> int:
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom_kind), "kernel": dom_kind,
                 "avg_launch_ms": round(avg_s * 1e3, 4)}
 
+    cio = None
+    if not args.no_cache_io:
+        cio = cache_io(kd, torch, idx, val, w.vocab)
+        log(f"cache io: {cio['bytes'] / 1e6:.1f} MB in {cio['shards']} shards; write {cio['write_gbs']:.2f} GB/s, "
+            f"loader to device {cio['load_gbs']:.2f} GB/s = {cio['load_tokens_per_s']:.0f} tokens/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         del h, wd, idx, val
@@ -309,7 +365,7 @@ def main() -> int:
         "config": {"workload": args.workload, "n_tokens": n, "d": w.d, "vocab": w.vocab, "k": k, "tau": w.tau,
                    "chunk_tokens": args.chunk or "default", "teacher": w.teacher},
         "mfma_util": round(mfma_util, 4), "peak_gb": round(peak_gb, 3),
-        "roofline": roof, "cpu_baseline": cpu, "cache_build": cache,
+        "roofline": roof, "cpu_baseline": cpu, "cache_build": cache, "cache_io": cio,
         "kernels_ms_per_step": {k2: round(s["total_ms"] / args.steps, 4) for k2, s in stats.items()},
     }
     print(json.dumps(line), flush=True)

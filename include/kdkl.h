@@ -86,7 +86,9 @@ typedef enum {
   KD_ERR_UNSUPPORTED_ARCH = 8,   /* the current device is not gfx950 */
   KD_ERR_LAUNCH = 9,             /* a kernel launch failed */
   KD_ERR_IDX_OUT_OF_RANGE = 10,  /* only with KD_CHECK=1: a cached index is outside [0, V) */
-  KD_ERR_TOPK_OVERFLOW = 11      /* only with KD_CHECK=1: too many near-ties at the K-th value */
+  KD_ERR_TOPK_OVERFLOW = 11,     /* only with KD_CHECK=1: too many near-ties at the K-th value */
+  KD_ERR_IO = 12,                /* kdcache.h: a file could not be opened, read or written */
+  KD_ERR_BAD_FORMAT = 13         /* kdcache.h: a shard header or file size does not match the format */
 } kd_status;
 
 typedef enum { KD_OP_TOPK_BUILD = 0, KD_OP_KL_FWD = 1, KD_OP_KL_BWD = 2 } kd_op;

@@ -14,6 +14,11 @@ Entry points (same names as the C ABI):
 * :func:`kd_chunked_kl_bwd` -- ``dH`` and ``dW``.
 * :class:`KDChunkedKL` / :func:`chunked_kl_loss` -- autograd wrapper (forward
   saves ``lse``; backward calls :func:`kd_chunked_kl_bwd`).
+* :func:`kd_cache_write`, :func:`kd_cache_info_read`, :func:`kd_cache_read` --
+  on-disk cache shards (C ABI in ``include/kdcache.h``);
+  :func:`kd_cache_loader_open` / :func:`kd_cache_loader_next` /
+  :func:`kd_cache_loader_close` and the iterator :class:`CacheLoader` -- streaming
+  of shards to the device with prefetch.
 """
 from __future__ import annotations
 
@@ -32,12 +37,15 @@ KD_OP_TOPK_BUILD, KD_OP_KL_FWD, KD_OP_KL_BWD = 0, 1, 2
 STATUS_NAMES = {
     0: "KD_OK", 1: "KD_ERR_NULL_POINTER", 2: "KD_ERR_BAD_SHAPE", 3: "KD_ERR_BAD_DTYPE", 4: "KD_ERR_BAD_TAU",
     5: "KD_ERR_MISALIGNED", 6: "KD_ERR_WORKSPACE_TOO_SMALL", 7: "KD_ERR_NO_DEVICE", 8: "KD_ERR_UNSUPPORTED_ARCH",
-    9: "KD_ERR_LAUNCH", 10: "KD_ERR_IDX_OUT_OF_RANGE", 11: "KD_ERR_TOPK_OVERFLOW",
+    9: "KD_ERR_LAUNCH", 10: "KD_ERR_IDX_OUT_OF_RANGE", 11: "KD_ERR_TOPK_OVERFLOW", 12: "KD_ERR_IO",
+    13: "KD_ERR_BAD_FORMAT",
 }
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd",
-            "kd_status_string", "kd_version", "kd_profile_begin", "kd_profile_end")
+            "kd_status_string", "kd_version", "kd_profile_begin", "kd_profile_end",
+            "kd_cache_write", "kd_cache_info_read", "kd_cache_read", "kd_cache_loader_open",
+            "kd_cache_loader_info", "kd_cache_loader_next", "kd_cache_loader_close")
 
 
 class KDProblem(ctypes.Structure):
@@ -63,6 +71,17 @@ class KDKernelStat(ctypes.Structure):
         ("total_ms", ctypes.c_double),
         ("flops", ctypes.c_double),
         ("bytes", ctypes.c_double),
+    ]
+
+
+class KDCacheInfo(ctypes.Structure):
+    """Mirror of ``kd_cache_info`` in include/kdcache.h."""
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("vocab", ctypes.c_int64),
+        ("k", ctypes.c_int32),
+        ("idx_bits", ctypes.c_int32),
+        ("val_dtype", ctypes.c_int32),
     ]
 
 
@@ -100,6 +119,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_profile_begin.restype = ctypes.c_int
     lib.kd_profile_end.argtypes = [ctypes.POINTER(KDKernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.kd_profile_end.restype = ctypes.c_int
+    CI = ctypes.POINTER(KDCacheInfo)
+    cp, i64, i32 = ctypes.c_char_p, ctypes.c_int64, ctypes.c_int32
+    lib.kd_cache_write.argtypes = [cp, CI, vp, vp]
+    lib.kd_cache_info_read.argtypes = [cp, CI]
+    lib.kd_cache_read.argtypes = [cp, i64, i64, vp, vp]
+    lib.kd_cache_loader_open.argtypes = [ctypes.POINTER(cp), i32, i64, i32, ctypes.POINTER(vp)]
+    lib.kd_cache_loader_info.argtypes = [vp, CI]
+    lib.kd_cache_loader_next.argtypes = [vp, vp, vp, ctypes.POINTER(i64), vp]
+    lib.kd_cache_loader_close.argtypes = [vp]
+    for f in ("kd_cache_write", "kd_cache_info_read", "kd_cache_read", "kd_cache_loader_open",
+              "kd_cache_loader_info", "kd_cache_loader_next", "kd_cache_loader_close"):
+        getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -267,3 +298,123 @@ class KDChunkedKL(torch.autograd.Function):
 
 def chunked_kl_loss(h, w, idx, val, tau: float = 1.0, chunk_tokens: int = 0) -> torch.Tensor:
     return KDChunkedKL.apply(h, w, idx, val, float(tau), int(chunk_tokens))
+
+
+# ---- on-disk cache shards and the streaming loader (include/kdcache.h)
+
+_VAL_TORCH = {KD_F32: torch.float32, KD_BF16: torch.bfloat16}
+
+
+def _host(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CPU tensor of dtype {dtype}")
+    return t
+
+
+def kd_cache_write(path: str, idx: torch.Tensor, val: torch.Tensor, vocab: int, idx_bits: int = 0) -> None:
+    """Write one shard from host tensors ``idx`` int32 [N,K] and ``val`` bf16/float32
+    [N,K].  ``idx_bits`` 0 picks 16 when ``vocab <= 65536``, else 32."""
+    if idx.dim() != 2 or val.shape != idx.shape:
+        raise ValueError("idx and val must both be [N, K]")
+    _host(idx, torch.int32, "idx")
+    vdt = _dt(val.dtype)
+    _host(val, val.dtype, "val")
+    info = KDCacheInfo(int(idx.shape[0]), int(vocab), int(idx.shape[1]), int(idx_bits), vdt)
+    _check(load_library().kd_cache_write(os.fsencode(path), ctypes.byref(info), _ptr(idx), _ptr(val)),
+           "kd_cache_write")
+
+
+def kd_cache_info_read(path: str) -> dict:
+    info = KDCacheInfo()
+    _check(load_library().kd_cache_info_read(os.fsencode(path), ctypes.byref(info)), "kd_cache_info_read")
+    return {"n_tokens": int(info.n_tokens), "vocab": int(info.vocab), "k": int(info.k),
+            "idx_bits": int(info.idx_bits), "val_dtype": int(info.val_dtype)}
+
+
+def kd_cache_read(path: str, row0: int = 0, rows: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Rows ``[row0, row0 + rows)`` of a shard as host tensors (idx int32, val)."""
+    info = kd_cache_info_read(path)
+    if rows is None:
+        rows = info["n_tokens"] - row0
+    idx = torch.empty((rows, info["k"]), dtype=torch.int32)
+    val = torch.empty((rows, info["k"]), dtype=_VAL_TORCH[info["val_dtype"]])
+    _check(load_library().kd_cache_read(os.fsencode(path), int(row0), int(rows), _ptr(idx), _ptr(val)),
+           "kd_cache_read")
+    return idx, val
+
+
+def kd_cache_loader_open(paths, batch_tokens: int, prefetch: int = 2) -> ctypes.c_void_p:
+    """Open a streaming loader over the shards ``paths`` (read in order)."""
+    enc = [os.fsencode(p) for p in paths]
+    arr = (ctypes.c_char_p * max(1, len(enc)))(*enc)
+    h = ctypes.c_void_p()
+    _check(load_library().kd_cache_loader_open(arr, len(enc), int(batch_tokens), int(prefetch), ctypes.byref(h)),
+           "kd_cache_loader_open")
+    return h
+
+
+def kd_cache_loader_info(handle: ctypes.c_void_p) -> dict:
+    info = KDCacheInfo()
+    _check(load_library().kd_cache_loader_info(handle, ctypes.byref(info)), "kd_cache_loader_info")
+    return {"n_tokens": int(info.n_tokens), "vocab": int(info.vocab), "k": int(info.k),
+            "idx_bits": int(info.idx_bits), "val_dtype": int(info.val_dtype)}
+
+
+def kd_cache_loader_next(handle: ctypes.c_void_p, idx_dev: torch.Tensor, val_dev: torch.Tensor) -> int:
+    """Enqueue the next batch's copies into the device tensors (on the current
+    stream of their device); returns its row count, 0 at the end."""
+    dev = _need_gpu(idx_dev, val_dev)
+    rows = ctypes.c_int64(0)
+    with torch.cuda.device(dev):
+        _check(load_library().kd_cache_loader_next(handle, _ptr(idx_dev), _ptr(val_dev), ctypes.byref(rows),
+                                                   _stream(dev)), "kd_cache_loader_next")
+    return int(rows.value)
+
+
+def kd_cache_loader_close(handle: ctypes.c_void_p) -> None:
+    _check(load_library().kd_cache_loader_close(handle), "kd_cache_loader_close")
+
+
+class CacheLoader:
+    """Iterates ``(idx, val)`` device tensors of ``batch_tokens`` rows (the last
+    batch may be shorter) over cache shards, prefetching in a background thread.
+    Each batch has its own device tensors, so a batch stays valid while the next
+    one streams in."""
+
+    def __init__(self, paths, batch_tokens: int, prefetch: int = 2, device: str = "cuda"):
+        self.device = torch.device(device)
+        self.handle = kd_cache_loader_open(paths, batch_tokens, prefetch)
+        self.info = kd_cache_loader_info(self.handle)
+        self.batch = int(batch_tokens)
+
+    def __iter__(self):
+        return self
+
+    def __next__(self) -> Tuple[torch.Tensor, torch.Tensor]:
+        if self.handle is None:
+            raise StopIteration
+        k = self.info["k"]
+        idx = torch.empty((self.batch, k), dtype=torch.int32, device=self.device)
+        val = torch.empty((self.batch, k), dtype=_VAL_TORCH[self.info["val_dtype"]], device=self.device)
+        rows = kd_cache_loader_next(self.handle, idx, val)
+        if rows == 0:
+            self.close()
+            raise StopIteration
+        return idx[:rows], val[:rows]
+
+    def close(self) -> None:
+        if self.handle is not None:
+            kd_cache_loader_close(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -12,6 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "kdkl.hip")
+SRC_CACHE = os.path.join(PKG, "csrc", "kdcache.cpp")
 OUT = os.path.join(PKG, "libkdkl.so")
 ARCH = "gfx950"
 
@@ -38,7 +39,7 @@ def build(verbose: bool = False) -> str:
     """Compile the library; returns the path of the shared object."""
     tmp = OUT + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           SRC, "-o", tmp]
+           SRC, SRC_CACHE, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

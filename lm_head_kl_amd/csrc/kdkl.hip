@@ -587,6 +587,8 @@ const char* kd_status_string(kd_status s) {
     case KD_ERR_LAUNCH: return "a kernel launch failed";
     case KD_ERR_IDX_OUT_OF_RANGE: return "a cached index is outside [0, V)";
     case KD_ERR_TOPK_OVERFLOW: return "too many near-ties at the K-th teacher logit";
+    case KD_ERR_IO: return "a cache file could not be opened, read or written";
+    case KD_ERR_BAD_FORMAT: return "a cache shard does not match the shard format";
   }
   return "unknown status";
 }

@@ -2,6 +2,7 @@
 the header declares, and every argument error is reported before any device
 work (so these run on a host without a GPU)."""
 import ctypes
+import glob
 import math
 import os
 import re
@@ -12,7 +13,7 @@ import pytest
 import lm_head_kl_amd as kd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kdkl.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -24,7 +25,7 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kd_\w+)\s*\(", text, flags=re.M)))
 

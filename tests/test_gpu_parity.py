@@ -5,6 +5,7 @@ loss is the oracle's exact top-K, so both sides see the same cache bytes.
 Sizes here are small enough for the oracle to finish in seconds while still
 spanning several 256 x 256 tiles and ragged tails in every dimension.
 """
+import os
 import numpy as np
 import pytest
 import torch
@@ -267,3 +268,35 @@ def test_autograd_function():
     torch.cuda.synchronize()
     assert rel_max_err(to_f64(h.grad), ref_dH) <= GRAD_TOL
     assert rel_max_err(to_f64(w.grad), ref_dW) <= GRAD_TOL
+
+
+def test_kd_check_reports_out_of_range_index():
+    """With KD_CHECK=1 (read once per process, hence a child process) the forward
+    synchronises and returns KD_ERR_IDX_OUT_OF_RANGE for an index outside [0, V);
+    a valid cache still succeeds."""
+    import subprocess
+    import sys
+    script = r'''
+import numpy as np, torch, sys
+import kd_synth, lm_head_kl_amd as kd
+p = kd_synth.small_problem(300, 64, 600, seed=6)
+to = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+h, w = to(p["H"]), to(p["W"])
+val = torch.zeros((300, 5), dtype=torch.bfloat16, device="cuda:0")
+idx = np.random.default_rng(1).integers(0, 600, size=(300, 5)).astype(np.int32)
+loss, _, _ = kd.kd_chunked_kl_fwd(h, w, torch.from_numpy(idx).to("cuda:0"), val, 1.0)
+assert np.isfinite(loss.item())
+idx[17, 2] = 600
+try:
+    kd.kd_chunked_kl_fwd(h, w, torch.from_numpy(idx).to("cuda:0"), val, 1.0)
+except kd.KDError as e:
+    assert e.status == 10, e.status
+    print("status", e.status)
+    sys.exit(0)
+sys.exit(3)
+'''
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, KD_CHECK="1", PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-c", script], env=env, cwd=root, stdout=subprocess.PIPE,
+                       stderr=subprocess.STDOUT, text=True, timeout=180)
+    assert r.returncode == 0 and "status 10" in r.stdout, r.stdout[-2000:]

@@ -13,6 +13,7 @@
 #include <unistd.h>
 
 #include <algorithm>
+#include <atomic>
 #include <condition_variable>
 #include <cstdint>
 #include <cstdio>
@@ -198,7 +199,10 @@ extern "C" kd_status kd_cache_write(const char* path, const kd_cache_info* info,
   put64(h + 48, (uint64_t)lay.idx_off);
   put64(h + 56, (uint64_t)lay.val_off);
 
-  const std::string tmp = std::string(path) + ".tmp." + std::to_string((long)::getpid());
+  // unique per process and per call, so concurrent writers never share a temporary
+  static std::atomic<unsigned long> serial{0};
+  const std::string tmp = std::string(path) + ".tmp." + std::to_string((long)::getpid()) + "." +
+                          std::to_string(serial.fetch_add(1));
   const int fd = ::open(tmp.c_str(), O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
   if (fd < 0) return KD_ERR_IO;
   bool ok = write_all(fd, h, kHeader);

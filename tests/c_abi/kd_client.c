@@ -1,13 +1,15 @@
 /*
  * Plain-C client of the kdkl C ABI (include/kdkl.h), linked against libkdkl.so and
  * the HIP runtime's C API only.  It reads a problem file, builds the teacher's
- * top-K cache, runs the forward and the backward, and writes the results:
+ * top-K cache, runs the forward and the backward, and writes the results.  It
+ * then writes the cache to two shard files in DIR (include/kdcache.h), streams them
+ * back to the device with the loader and runs the forward again on that copy:
  *
- *   kd_client IN OUT
+ *   kd_client IN OUT DIR
  *   IN : int64 N, d, V; int32 K; float tau; then H [N*d], W [V*d], W_T [V*d] as bf16
  *        bits (uint16), teacher hidden states = H
  *   OUT: int32 status; then idx [N*K] int32, val [N*K] bf16 bits, loss float,
- *        lse [N] float, dH [N*d] float, dW [V*d] float
+ *        lse [N] float, dH [N*d] float, dW [V*d] float, loss from the reloaded cache float
  *
  * Exit status 0 on success; on a library error the kd_status is printed with
  * kd_status_string() and the exit status is 1.
@@ -16,7 +18,9 @@
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
+#include "kdcache.h"
 #include "kdkl.h"
 
 #define HIP_OK(x)                                                             \
@@ -40,8 +44,8 @@ static int read_all(FILE* f, void* p, size_t n) { return fread(p, 1, n, f) == n;
 static int write_all(FILE* f, const void* p, size_t n) { return fwrite(p, 1, n, f) == n; }
 
 int main(int argc, char** argv) {
-  if (argc != 3) {
-    fprintf(stderr, "usage: kd_client IN OUT\n");
+  if (argc != 4) {
+    fprintf(stderr, "usage: kd_client IN OUT DIR\n");
     return 2;
   }
   FILE* fi = fopen(argv[1], "rb");
@@ -106,12 +110,46 @@ int main(int argc, char** argv) {
   HIP_OK(hipMemcpy(dhh, ddh, 4 * nh, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(dwh, ddw, 4 * nw, hipMemcpyDeviceToHost));
 
+  /* the cache through two shard files and the loader, then the forward again */
+  char path0[4096], path1[4096];
+  snprintf(path0, sizeof path0, "%s/c0.kdc", argv[3]);
+  snprintf(path1, sizeof path1, "%s/c1.kdc", argv[3]);
+  const int64_t half = N / 2;
+  kd_cache_info ci0 = {half, V, K, 0, KD_BF16};
+  kd_cache_info ci1 = {N - half, V, K, 0, KD_BF16};
+  KD_OK_OR_FAIL(kd_cache_write(path0, &ci0, idx, val));
+  KD_OK_OR_FAIL(kd_cache_write(path1, &ci1, idx + half * K, val + half * K));
+  void *didx2, *dval2, *dloss2;
+  HIP_OK(hipMalloc(&didx2, 4 * nk + 16));
+  HIP_OK(hipMalloc(&dval2, 2 * nk + 16));
+  HIP_OK(hipMalloc(&dloss2, 16));
+  const char* paths[2] = {path0, path1};
+  kd_cache_loader* ld = NULL;
+  const int64_t batch = N / 3 + 1;
+  KD_OK_OR_FAIL(kd_cache_loader_open(paths, 2, batch, 2, &ld));
+  int64_t row = 0, rows = 0;
+  do {
+    KD_OK_OR_FAIL(kd_cache_loader_next(ld, (int32_t*)didx2 + row * K, (uint16_t*)dval2 + row * K, &rows, st));
+    row += rows;
+  } while (rows > 0);
+  HIP_OK(hipStreamSynchronize(st));
+  KD_OK_OR_FAIL(kd_cache_loader_close(ld));
+  if (row != N) {
+    fprintf(stderr, "kd_client: loader returned %lld rows, expected %lld\n", (long long)row, (long long)N);
+    return 1;
+  }
+  KD_OK_OR_FAIL(kd_chunked_kl_fwd(&p, dh_in, dw_in, (const int32_t*)didx2, dval2, (float*)dloss2, (float*)dlse,
+                                  NULL, dws, ws_bytes, st));
+  HIP_OK(hipStreamSynchronize(st));
+  float loss2 = 0.f;
+  HIP_OK(hipMemcpy(&loss2, dloss2, 4, hipMemcpyDeviceToHost));
+
   FILE* fo = fopen(argv[2], "wb");
   if (!fo) return 2;
   const int32_t ok = 0;
   if (!write_all(fo, &ok, 4) || !write_all(fo, idx, 4 * nk) || !write_all(fo, val, 2 * nk) ||
       !write_all(fo, &loss, 4) || !write_all(fo, lse, 4 * (size_t)N) || !write_all(fo, dhh, 4 * nh) ||
-      !write_all(fo, dwh, 4 * nw))
+      !write_all(fo, dwh, 4 * nw) || !write_all(fo, &loss2, 4))
     return 2;
   fclose(fo);
   printf("kd_client: N=%lld d=%lld V=%lld K=%d loss=%.6f (kd_version %d)\n", (long long)N, (long long)d,

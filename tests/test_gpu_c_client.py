@@ -1,7 +1,9 @@
 """The C ABI from plain C: tests/c_abi/kd_client (built by the package's build step
 with gcc against libkdkl.so and the HIP runtime's C API, no torch) builds the
 teacher cache, runs the forward and the backward; its outputs must match the
-float64 oracle on the same inputs."""
+float64 oracle on the same inputs.  It also writes the cache to shard files and
+streams them back with the loader (include/kdcache.h): the loss from that copy must
+be the same float."""
 import os
 import subprocess
 
@@ -29,7 +31,7 @@ def test_c_client_matches_oracle(tmp_path):
         for a in (p["H"], p["W"], p["WT"]):
             f.write(np.ascontiguousarray(a).view(np.uint16).tobytes())
     print(f"[c-client] N={n} d={d} V={v} K={k}", flush=True)
-    r = subprocess.run([CLIENT, str(inp), str(out)], capture_output=True, text=True, timeout=120)
+    r = subprocess.run([CLIENT, str(inp), str(out), str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     buf = open(out, "rb").read()
     off = 0
@@ -47,7 +49,10 @@ def test_c_client_matches_oracle(tmp_path):
     g_lse = take(np.float32, n)
     g_dh = take(np.float32, n * d).reshape(n, d)
     g_dw = take(np.float32, v * d).reshape(v, d)
+    g_loss2 = take(np.float32, 1)[0]
     assert off == len(buf)
+    assert np.float32(g_loss) == g_loss2                 # same cache bytes, same loss
+    assert (tmp_path / "c0.kdc").exists() and (tmp_path / "c1.kdc").exists()
 
     H = kd_synth.to_float64(p["H"], "bf16")
     W = kd_synth.to_float64(p["W"], "bf16")

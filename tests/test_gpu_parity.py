@@ -25,6 +25,8 @@ SHAPES = [
     (64, 64, 300, 1, "bf16", 0.5),
     (700, 128, 2600, 100, "f32", 1.5),
     (257, 512, 4099, 64, "bf16", 1.0),
+    (1, 8, 50, 50, "bf16", 1.0),          # one token, the smallest d, K = V inside one tile
+    (33, 8, 257, 5, "f32", 0.7),          # vocabulary one past a tile
 ]
 
 

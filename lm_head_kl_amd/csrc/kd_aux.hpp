@@ -83,6 +83,42 @@ __global__ void __launch_bounds__(1024) bucket_kernel(const int32_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// float64 dot product of an h row and a w row of length d (a multiple of 8), by one
+// wave: lane l sums the 16-byte chunks l, l + 64, ... in ascending order, then a
+// butterfly over the wave, so every lane returns the same value and the order never
+// depends on timing.  Up to 8 chunks per lane are loaded before any is used, which
+// keeps 8 row segments per wave in flight (the w rows come from HBM at random).
+template <typename T>
+__device__ __forceinline__ double wave_dot_f64(const T* __restrict__ h, const T* __restrict__ w, int d, int lane) {
+  constexpr int EPC = 16 / int(sizeof(T));
+  constexpr int U = 8;
+  double acc = 0.0;
+  for (int j0 = lane * EPC; j0 < d; j0 += U * 64 * EPC) {
+    u32x4 hv[U], wv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * 64 * EPC;
+      if (j < d) {
+        hv[u] = *(const u32x4*)(h + j);
+        wv[u] = *(const u32x4*)(w + j);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u * 64 * EPC < d) {
+        const T* hp = (const T*)&hv[u];
+        const T* wp = (const T*)&wv[u];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc = fma((double)to_f32<T>(hp[e]), (double)to_f32<T>(wp[e]), acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
 // Block sum of one double per thread (256 threads), fixed order.
 __device__ __forceinline__ double block_sum_256(double v, double* sh) {
   sh[threadIdx.x] = v;
@@ -452,20 +488,8 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
     return;
   }
   // float64 re-scoring: one wave per candidate, lanes split d in 16-byte chunks
-  constexpr int EPC = 16 / int(sizeof(T));
   for (int c = wave; c < C; c += SEL_THREADS / 64) {
-    const T* w = wt + (int64_t)cidx[c] * d;
-    double acc = 0.0;
-    for (int j = lane * EPC; j < d; j += 64 * EPC) {
-      const u32x4 hv = *(const u32x4*)(h + j);
-      const u32x4 wv = *(const u32x4*)(w + j);
-      const T* hp = (const T*)&hv;
-      const T* wp = (const T*)&wv;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc = fma((double)to_f32<T>(hp[e]), (double)to_f32<T>(wp[e]), acc);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    const double acc = wave_dot_f64<T>(h, wt + (int64_t)cidx[c] * d, d, lane);
     if (lane == 0) cscore[c] = acc;
   }
   __syncthreads();
@@ -574,20 +598,8 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_fast_kernel(
     return;
   }
   // 3. float64 re-scoring: one wave per candidate, lanes split d in 16-byte chunks
-  constexpr int EPC = 16 / int(sizeof(T));
   for (int c = wave; c < C; c += SEL_THREADS / 64) {
-    const T* w = wt + (int64_t)cidx[c] * d;
-    double acc = 0.0;
-    for (int j = lane * EPC; j < d; j += 64 * EPC) {
-      const u32x4 hv = *(const u32x4*)(h + j);
-      const u32x4 wv = *(const u32x4*)(w + j);
-      const T* hp = (const T*)&hv;
-      const T* wp = (const T*)&wv;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc = fma((double)to_f32<T>(hp[e]), (double)to_f32<T>(wp[e]), acc);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    const double acc = wave_dot_f64<T>(h, wt + (int64_t)cidx[c] * d, d, lane);
     if (lane == 0) cscore[c] = acc;
   }
   __syncthreads();

@@ -2,7 +2,6 @@
 boundaries arrive bit-exact, prefetch slots are reused only after their copies, and
 the loss computed from a cache that went through the files equals the loss from the
 cache as built (same bytes in, same result out)."""
-import os
 
 import pytest
 import torch

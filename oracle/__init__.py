@@ -26,8 +26,9 @@ Every function here materialises full logit rows (in row blocks) in float64 on
 the exact stored input values.  Readings where the pages are silent are listed
 in each function's docstring.
 
-Pins: each function is checked in ``tests/test_oracle_pins.py`` against closed
-forms, library routines, brute force and finite differences.  No function here
+Pins: each function is checked in ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_variant_pins.py`` against closed forms, library routines,
+brute force and finite differences.  No function here
 is "parity unpinned".
 """
 from .kl import (  # noqa: F401
@@ -39,3 +40,4 @@ from .kl import (  # noqa: F401
     kl_dense_reconstruction,
 )
 from .topk import topk_cache, round_to_bf16, bf16_bits  # noqa: F401
+from .variants import counted_rows, variant_forward, variant_backward  # noqa: F401

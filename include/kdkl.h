@@ -25,7 +25,8 @@
  *   idx [N, K] int32 cached vocabulary indices        (row-major)
  *   val [N, K] cached teacher logits                   (row-major)
  *
- * What is computed (all rows count; mean over N):
+ * What is computed by the plain calls (all rows count; mean over N; a padding
+ * mask and a hard-label mix are the _ex calls below):
  *   z[i,v]  = H[i,:] . W[v,:]                 student logits (never stored)
  *   lse[i]  = log sum_v exp(z[i,v])           over the whole vocabulary
  *   p[i,k]  = softmax_k(val[i,k] / tau)       teacher renormalised over its K entries
@@ -85,10 +86,11 @@ typedef enum {
   KD_ERR_NO_DEVICE = 7,          /* no HIP device is current */
   KD_ERR_UNSUPPORTED_ARCH = 8,   /* the current device is not gfx950 */
   KD_ERR_LAUNCH = 9,             /* a kernel launch failed */
-  KD_ERR_IDX_OUT_OF_RANGE = 10,  /* only with KD_CHECK=1: a cached index is outside [0, V) */
+  KD_ERR_IDX_OUT_OF_RANGE = 10,  /* only with KD_CHECK=1: a cached index (or mixed-in label) is outside [0, V) */
   KD_ERR_TOPK_OVERFLOW = 11,     /* only with KD_CHECK=1: too many near-ties at the K-th value */
   KD_ERR_IO = 12,                /* kdcache.h: a file could not be opened, read or written */
-  KD_ERR_BAD_FORMAT = 13         /* kdcache.h: a shard header or file size does not match the format */
+  KD_ERR_BAD_FORMAT = 13,        /* kdcache.h: a shard header or file size does not match the format */
+  KD_ERR_BAD_OPTION = 14         /* a kd_loss_opts field is outside its domain */
 } kd_status;
 
 typedef enum { KD_OP_TOPK_BUILD = 0, KD_OP_KL_FWD = 1, KD_OP_KL_BWD = 2 } kd_op;
@@ -152,6 +154,44 @@ kd_status kd_chunked_kl_bwd(const kd_problem* p, const void* h, const void* w,
                             const float* lse, const float* grad_loss,
                             void* dh_out, float* dw_out,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Loss variants: a padding mask and a hard-label cross-entropy mix.
+ * The paper's abstract ([abs]) reports ablations of the loss design and of
+ * sequence packing without defining them. These calls give the plain reading of
+ * both in next-token training, on top of the KL above (a = ce_weight, y = labels):
+ *   C       = { i : y[i] != ignore_index }   rows that count (every row when labels is NULL)
+ *   CE[i]   = lse[i] - z[i, y[i]]            cross-entropy with the hard label
+ *   l[i]    = (1 - a) KL[i] + a CE[i] for i in C, 0 for the other rows
+ *   loss    = (1/|C|) sum_i l[i]             (0 when no row counts)
+ *   dZ[i,v] = (g/|C|) (exp(z[i,v] - lse[i]) - (1 - a) sum_{k: idx[i,k]=v} p[i,k] - a [v = y[i]])
+ *             for i in C; dZ[i,:] = 0 for the other rows
+ * An ignored row's cache entries (idx, val) are not read, so padding may hold
+ * anything there; its lse is still computed. With a = 0 the labels only mask.
+ * With a > 0, a label outside [0, V) other than ignore_index makes its row's
+ * term NaN (KD_CHECK=1: KD_ERR_IDX_OUT_OF_RANGE), like a cached index. */
+typedef struct {
+  const int32_t* labels;  /* [N] int32 DEVICE array (4-byte aligned), or NULL */
+  int32_t ignore_index;   /* label value of a row left out (e.g. -100 for padding) */
+  float ce_weight;        /* a in [0, 1]; > 0 needs labels */
+} kd_loss_opts;
+
+/* kd_chunked_kl_fwd with loss options (NULL = kd_chunked_kl_fwd). rows_out [N]
+ * (or NULL) receives l[i]; loss_out the mean over the counted rows.
+ * KD_ERR_BAD_OPTION: ce_weight not finite or outside [0, 1], or > 0 without labels.
+ * Workspace: kd_workspace_size(KD_OP_KL_FWD, ...), the same as the plain call. */
+kd_status kd_chunked_kl_fwd_ex(const kd_problem* p, const kd_loss_opts* opts, const void* h, const void* w,
+                               const int32_t* idx, const void* val,
+                               float* loss_out, float* lse_out, float* rows_out,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* kd_chunked_kl_bwd with loss options (NULL = kd_chunked_kl_bwd); `opts` must
+ * match the forward call that produced `lse`. dH rows of ignored tokens are 0.
+ * Workspace: kd_workspace_size(KD_OP_KL_BWD, ...), the same as the plain call. */
+kd_status kd_chunked_kl_bwd_ex(const kd_problem* p, const kd_loss_opts* opts, const void* h, const void* w,
+                               const int32_t* idx, const void* val,
+                               const float* lse, const float* grad_loss,
+                               void* dh_out, float* dw_out,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* kd_status_string(kd_status s);

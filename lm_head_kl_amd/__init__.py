@@ -12,6 +12,9 @@ Entry points (same names as the C ABI):
   logit) pairs of ``H_T @ W_T^T`` per token.
 * :func:`kd_chunked_kl_fwd` -- loss, per-row log-sum-exp (and per-row KL).
 * :func:`kd_chunked_kl_bwd` -- ``dH`` and ``dW``.
+  Both take optional ``labels`` / ``ignore_index`` / ``ce_weight`` (a padding
+  mask and a hard-label cross-entropy mix), which select the C calls
+  ``kd_chunked_kl_fwd_ex`` / ``kd_chunked_kl_bwd_ex``.
 * :class:`KDChunkedKL` / :func:`chunked_kl_loss` -- autograd wrapper (forward
   saves ``lse``; backward calls :func:`kd_chunked_kl_bwd`).
 * :func:`kd_cache_write`, :func:`kd_cache_info_read`, :func:`kd_cache_read` --
@@ -38,12 +41,12 @@ STATUS_NAMES = {
     0: "KD_OK", 1: "KD_ERR_NULL_POINTER", 2: "KD_ERR_BAD_SHAPE", 3: "KD_ERR_BAD_DTYPE", 4: "KD_ERR_BAD_TAU",
     5: "KD_ERR_MISALIGNED", 6: "KD_ERR_WORKSPACE_TOO_SMALL", 7: "KD_ERR_NO_DEVICE", 8: "KD_ERR_UNSUPPORTED_ARCH",
     9: "KD_ERR_LAUNCH", 10: "KD_ERR_IDX_OUT_OF_RANGE", 11: "KD_ERR_TOPK_OVERFLOW", 12: "KD_ERR_IO",
-    13: "KD_ERR_BAD_FORMAT",
+    13: "KD_ERR_BAD_FORMAT", 14: "KD_ERR_BAD_OPTION",
 }
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd",
-            "kd_status_string", "kd_version", "kd_profile_begin", "kd_profile_end",
+            "kd_chunked_kl_fwd_ex", "kd_chunked_kl_bwd_ex", "kd_status_string", "kd_version", "kd_profile_begin", "kd_profile_end",
             "kd_cache_write", "kd_cache_info_read", "kd_cache_read", "kd_cache_loader_open",
             "kd_cache_loader_info", "kd_cache_loader_next", "kd_cache_loader_close")
 
@@ -60,6 +63,15 @@ class KDProblem(ctypes.Structure):
         ("val_dtype", ctypes.c_int32),
         ("dh_dtype", ctypes.c_int32),
         ("chunk_tokens", ctypes.c_int32),
+    ]
+
+
+class KDLossOpts(ctypes.Structure):
+    """Mirror of ``kd_loss_opts``."""
+    _fields_ = [
+        ("labels", ctypes.c_void_p),
+        ("ignore_index", ctypes.c_int32),
+        ("ce_weight", ctypes.c_float),
     ]
 
 
@@ -109,7 +121,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_topk_cache_build.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd"):
+    O = ctypes.POINTER(KDLossOpts)
+    lib.kd_chunked_kl_fwd_ex.argtypes = [P, O, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_chunked_kl_bwd_ex.argtypes = [P, O, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd",
+              "kd_chunked_kl_fwd_ex", "kd_chunked_kl_bwd_ex"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
@@ -215,11 +231,26 @@ def kd_topk_cache_build(h_t: torch.Tensor, w_t: torch.Tensor, k: int, chunk_toke
     return idx, val
 
 
+def _opts(labels: Optional[torch.Tensor], ignore_index: int, ce_weight: float, n: int
+          ) -> Optional[KDLossOpts]:
+    """The loss options, or None for the plain loss (no labels and no mix)."""
+    if labels is None and ce_weight == 0.0:
+        return None
+    if labels is not None and (labels.dtype != torch.int32 or labels.shape != (n,)):
+        raise ValueError("labels must be int32 [N]")
+    return KDLossOpts(_ptr(labels), int(ignore_index), float(ce_weight))
+
+
 def kd_chunked_kl_fwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, tau: float,
-                      with_rows: bool = False, chunk_tokens: int = 0
+                      with_rows: bool = False, chunk_tokens: int = 0, labels: Optional[torch.Tensor] = None,
+                      ignore_index: int = -100, ce_weight: float = 0.0
                       ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
-    """Returns ``(loss [] float32, lse [N] float32, kl_rows [N] float32 or None)``."""
-    dev = _need_gpu(h, w, idx, val)
+    """Returns ``(loss [] float32, lse [N] float32, rows [N] float32 or None)``.
+
+    With ``labels`` (int32 [N]), rows labelled ``ignore_index`` are left out and
+    the mean runs over the others; ``ce_weight`` a mixes in the cross-entropy
+    with the labels: row term ``(1 - a) KL + a CE`` (``rows`` holds those terms)."""
+    dev = _need_gpu(h, w, idx, val, labels)
     n, d = h.shape
     v = w.shape[0]
     k = idx.shape[1]
@@ -231,19 +262,28 @@ def kd_chunked_kl_fwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: 
     lse = torch.empty((n,), dtype=torch.float32, device=dev)
     rows = torch.empty((n,), dtype=torch.float32, device=dev) if with_rows else None
     ws = _workspace(KD_OP_KL_FWD, prob, dev)
+    opts = _opts(labels, ignore_index, ce_weight, n)
+    lib = load_library()
     with torch.cuda.device(dev):
-        _check(load_library().kd_chunked_kl_fwd(ctypes.byref(prob), _ptr(h), _ptr(w), _ptr(idx), _ptr(val),
-                                                _ptr(loss), _ptr(lse), _ptr(rows), _ptr(ws), ws.numel(),
-                                                _stream(dev)), "kd_chunked_kl_fwd")
+        if opts is None:
+            _check(lib.kd_chunked_kl_fwd(ctypes.byref(prob), _ptr(h), _ptr(w), _ptr(idx), _ptr(val), _ptr(loss),
+                                         _ptr(lse), _ptr(rows), _ptr(ws), ws.numel(), _stream(dev)),
+                   "kd_chunked_kl_fwd")
+        else:
+            _check(lib.kd_chunked_kl_fwd_ex(ctypes.byref(prob), ctypes.byref(opts), _ptr(h), _ptr(w), _ptr(idx),
+                                            _ptr(val), _ptr(loss), _ptr(lse), _ptr(rows), _ptr(ws), ws.numel(),
+                                            _stream(dev)), "kd_chunked_kl_fwd_ex")
     return loss, lse, rows
 
 
 def kd_chunked_kl_bwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, tau: float,
                       lse: torch.Tensor, grad: Optional[torch.Tensor] = None, dh_dtype: torch.dtype = torch.float32,
-                      chunk_tokens: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+                      chunk_tokens: int = 0, labels: Optional[torch.Tensor] = None, ignore_index: int = -100,
+                      ce_weight: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Returns ``(dH [N,d] dh_dtype, dW [V,d] float32)`` for upstream gradient
-    ``grad`` (a device scalar; None means 1)."""
-    dev = _need_gpu(h, w, idx, val, lse, grad)
+    ``grad`` (a device scalar; None means 1).  ``labels`` / ``ignore_index`` /
+    ``ce_weight`` must be those of the forward call."""
+    dev = _need_gpu(h, w, idx, val, lse, grad, labels)
     n, d = h.shape
     v = w.shape[0]
     k = idx.shape[1]
@@ -253,10 +293,17 @@ def kd_chunked_kl_bwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: 
     dh = torch.empty((n, d), dtype=dh_dtype, device=dev)
     dw = torch.empty((v, d), dtype=torch.float32, device=dev)
     ws = _workspace(KD_OP_KL_BWD, prob, dev)
+    opts = _opts(labels, ignore_index, ce_weight, n)
+    lib = load_library()
     with torch.cuda.device(dev):
-        _check(load_library().kd_chunked_kl_bwd(ctypes.byref(prob), _ptr(h), _ptr(w), _ptr(idx), _ptr(val),
-                                                _ptr(lse), _ptr(grad), _ptr(dh), _ptr(dw), _ptr(ws), ws.numel(),
-                                                _stream(dev)), "kd_chunked_kl_bwd")
+        if opts is None:
+            _check(lib.kd_chunked_kl_bwd(ctypes.byref(prob), _ptr(h), _ptr(w), _ptr(idx), _ptr(val), _ptr(lse),
+                                         _ptr(grad), _ptr(dh), _ptr(dw), _ptr(ws), ws.numel(), _stream(dev)),
+                   "kd_chunked_kl_bwd")
+        else:
+            _check(lib.kd_chunked_kl_bwd_ex(ctypes.byref(prob), ctypes.byref(opts), _ptr(h), _ptr(w), _ptr(idx),
+                                            _ptr(val), _ptr(lse), _ptr(grad), _ptr(dh), _ptr(dw), _ptr(ws),
+                                            ws.numel(), _stream(dev)), "kd_chunked_kl_bwd_ex")
     return dh, dw
 
 
@@ -276,28 +323,38 @@ def profile_end() -> dict:
 
 
 class KDChunkedKL(torch.autograd.Function):
-    """``loss = KDChunkedKL.apply(H, W, idx, val, tau)``; gradients flow to H and W."""
+    """``loss = KDChunkedKL.apply(H, W, idx, val, tau[, chunk_tokens, labels,
+    ignore_index, ce_weight])``; gradients flow to H and W."""
 
     @staticmethod
-    def forward(ctx, h, w, idx, val, tau, chunk_tokens=0):
-        loss, lse, _ = kd_chunked_kl_fwd(h, w, idx, val, tau, chunk_tokens=chunk_tokens)
-        ctx.save_for_backward(h, w, idx, val, lse)
+    def forward(ctx, h, w, idx, val, tau, chunk_tokens=0, labels=None, ignore_index=-100, ce_weight=0.0):
+        loss, lse, _ = kd_chunked_kl_fwd(h, w, idx, val, tau, chunk_tokens=chunk_tokens, labels=labels,
+                                         ignore_index=ignore_index, ce_weight=ce_weight)
+        ctx.save_for_backward(h, w, idx, val, lse, labels)
         ctx.tau = tau
         ctx.chunk_tokens = chunk_tokens
+        ctx.ignore_index = ignore_index
+        ctx.ce_weight = ce_weight
         return loss
 
     @staticmethod
     def backward(ctx, g):
-        h, w, idx, val, lse = ctx.saved_tensors
+        h, w, idx, val, lse, labels = ctx.saved_tensors
         g = g.detach().to(torch.float32).reshape(()).contiguous()
         dh, dw = kd_chunked_kl_bwd(h, w, idx, val, ctx.tau, lse, g,
                                    dh_dtype=torch.float32 if h.dtype == torch.float32 else torch.bfloat16,
-                                   chunk_tokens=ctx.chunk_tokens)
-        return dh.to(h.dtype), dw.to(w.dtype), None, None, None, None
+                                   chunk_tokens=ctx.chunk_tokens, labels=labels, ignore_index=ctx.ignore_index,
+                                   ce_weight=ctx.ce_weight)
+        return dh.to(h.dtype), dw.to(w.dtype), None, None, None, None, None, None, None
 
 
-def chunked_kl_loss(h, w, idx, val, tau: float = 1.0, chunk_tokens: int = 0) -> torch.Tensor:
-    return KDChunkedKL.apply(h, w, idx, val, float(tau), int(chunk_tokens))
+def chunked_kl_loss(h, w, idx, val, tau: float = 1.0, chunk_tokens: int = 0, labels=None,
+                    ignore_index: int = -100, ce_weight: float = 0.0) -> torch.Tensor:
+    """Mean top-K KL over the tokens (autograd).  ``labels`` (int32 [N]) leave out
+    the rows labelled ``ignore_index``; ``ce_weight`` mixes in the cross-entropy
+    with the labels."""
+    return KDChunkedKL.apply(h, w, idx, val, float(tau), int(chunk_tokens), labels, int(ignore_index),
+                             float(ce_weight))
 
 
 # ---- on-disk cache shards and the streaming loader (include/kdcache.h)

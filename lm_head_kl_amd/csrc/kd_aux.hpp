@@ -34,22 +34,47 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh /* >= 32 ints */, 
 // Bucket the cache entries of one 256-token tile by 256-wide vocabulary tile, so
 // the forward GEMM epilogue of tile (tx, ty) reads exactly the entries that fall
 // inside it.  Entry = token (8 bits) | vocab within tile (8 bits) | k (16 bits).
-// Out-of-range indices are skipped and flagged.
-__global__ void __launch_bounds__(1024) bucket_kernel(const int32_t* __restrict__ idx, int nr, int kc, int vocab,
-                                                      int n_ty, uint32_t* __restrict__ entries,
-                                                      int* __restrict__ offsets, int* __restrict__ bad) {
+// Out-of-range indices are skipped and flagged.  With labels, a row whose label
+// equals `ignore` contributes no entry (its cache row is not read), and with
+// add_label every other row's label is one more entry, k = kc.  Rows of entries
+// are kz apart (kc, or kc + 1 with add_label).
+__global__ void __launch_bounds__(1024) bucket_kernel(const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ labels, int ignore,
+                                                      int add_label, int nr, int kc, int kz, int vocab, int n_ty,
+                                                      uint32_t* __restrict__ entries, int* __restrict__ offsets,
+                                                      int* __restrict__ bad) {
   extern __shared__ int hist[];   // n_ty + 64 ints
+  __shared__ int lab[BX];
   int* sh = hist + n_ty + 1;
   const int tx = blockIdx.x;
   const int r0 = tx * BX;
   const int rows = min(BX, nr - r0);
   const int total = rows * kc;
+  const int all = total + (add_label ? rows : 0);
+  const bool masked = labels != nullptr;
   const int32_t* src = idx + (int64_t)r0 * kc;
   for (int b = threadIdx.x; b <= n_ty; b += blockDim.x) hist[b] = 0;
+  if (masked)
+    for (int t = threadIdx.x; t < rows; t += blockDim.x) lab[t] = labels[r0 + t];
   __syncthreads();
+  // entry e: cache entry (t, k) for e < total, else the label of row e - total;
+  // false for a row left out, else its vocabulary index in v
+  auto entry = [&](int e, int& v, int& t, int& k) -> bool {
+    if (e < total) {
+      t = e / kc;
+      k = e - t * kc;
+    } else {
+      t = e - total;
+      k = kc;
+    }
+    if (masked && lab[t] == ignore) return false;
+    v = e < total ? src[e] : lab[t];
+    return true;
+  };
   int nbad = 0;
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    const int v = src[e];
+  for (int e = threadIdx.x; e < all; e += blockDim.x) {
+    int v, t, k;
+    if (!entry(e, v, t, k)) continue;
     if ((unsigned)v < (unsigned)vocab) atomicAdd(&hist[v >> 8], 1);
     else ++nbad;
   }
@@ -71,12 +96,11 @@ __global__ void __launch_bounds__(1024) bucket_kernel(const int32_t* __restrict_
   }
   if (threadIdx.x == 0) out[n_ty] = tot;
   __syncthreads();
-  uint32_t* dst = entries + (int64_t)tx * BX * kc;
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    const int v = src[e];
-    if ((unsigned)v < (unsigned)vocab) {
+  uint32_t* dst = entries + (int64_t)tx * BX * kz;
+  for (int e = threadIdx.x; e < all; e += blockDim.x) {
+    int v, t, k;
+    if (entry(e, v, t, k) && (unsigned)v < (unsigned)vocab) {
       const int pos = atomicAdd(&hist[v >> 8], 1);
-      const int t = e / kc, k = e - t * kc;
       dst[pos] = uint32_t(t) | (uint32_t(v & 255) << 8) | (uint32_t(k) << 16);
     }
   }
@@ -170,14 +194,19 @@ __device__ __forceinline__ float row_max(float v, float* sh) {
 
 // Merge the per-tile (max, sum exp) partials of each row into lse, form the
 // teacher softmax over the K cached logits and the row's KL, and sum the block's
-// KL values (float64) for the deterministic loss reduction.  RB_ROWS rows per
+// row losses (float64) for the deterministic loss reduction.  RB_ROWS rows per
 // block, RB_TPR threads per row striding the vocabulary tiles (partials of
 // consecutive rows are adjacent, so a wave's loads are coalesced over rows).
+// With labels: a row whose label equals `ignore` gets lse only (loss term 0, its
+// cache row unread); with alpha > 0 the row's term is (1 - alpha) KL + alpha CE,
+// CE = lse - z[label], the label's logit gathered at k = kc (rows of zg are kz
+// apart).
 template <typename VT>
 __global__ void __launch_bounds__(256) merge_kernel(const float2* __restrict__ partials, int64_t ld_part, int n_ty,
                                                     const int32_t* __restrict__ idx, const VT* __restrict__ val,
-                                                    const float* __restrict__ zg, int nr, int kc, int vocab,
-                                                    float inv_tau, float* __restrict__ lse_out,
+                                                    const float* __restrict__ zg, int nr, int kc, int kz, int vocab,
+                                                    float inv_tau, const int32_t* __restrict__ labels, int ignore,
+                                                    float alpha, float* __restrict__ lse_out,
                                                     float* __restrict__ kl_out, double* __restrict__ block_sums) {
   __shared__ float sh[4 * RB_ROWS];
   __shared__ float2 shp[4 * RB_ROWS];
@@ -185,6 +214,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const float2* __restrict__ p
   const int r = threadIdx.x & (RB_ROWS - 1), q = threadIdx.x / RB_ROWS;
   const int t = blockIdx.x * RB_ROWS + r;
   const bool valid = t < nr;
+  const bool counted = valid && (labels == nullptr || labels[t] != ignore);
   // (1) log-sum-exp over the vocabulary tiles
   float M = -INFINITY, S = 0.f;
   if (valid)
@@ -205,17 +235,17 @@ __global__ void __launch_bounds__(256) merge_kernel(const float2* __restrict__ p
   // (2) teacher softmax over the K cached logits and the row's KL
   const VT* vr = val + (int64_t)t * kc;
   const int32_t* ir = idx + (int64_t)t * kc;
-  const float* zr = zg + (int64_t)t * kc;
+  const float* zr = zg + (int64_t)t * kz;
   float vmax = -INFINITY;
-  if (valid)
+  if (counted)
     for (int k = q; k < kc; k += RB_TPR) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
   vmax = row_max(vmax, sh);
   float Z = 0.f;
-  if (valid)
+  if (counted)
     for (int k = q; k < kc; k += RB_TPR) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
   const float logZ = logf(row_sum(Z, sh));
   float kl = 0.f;
-  if (valid)
+  if (counted)
     for (int k = q; k < kc; k += RB_TPR) {
       const float lp = to_f32<VT>(vr[k]) * inv_tau - vmax - logZ;
       const float p = expf(lp);
@@ -224,10 +254,19 @@ __global__ void __launch_bounds__(256) merge_kernel(const float2* __restrict__ p
     }
   kl = row_sum(kl, sh);
   if (q == 0) {
-    klrow[r] = valid ? kl : 0.f;
+    float l = 0.f;
+    if (counted) {
+      l = kl;
+      if (alpha > 0.f) {
+        const int y = labels[t];
+        const float ce = (unsigned)y < (unsigned)vocab ? lse - zr[kc] : NAN;
+        l = (1.f - alpha) * kl + alpha * ce;
+      }
+    }
+    klrow[r] = l;
     if (valid) {
       lse_out[t] = lse;
-      if (kl_out) kl_out[t] = kl;
+      if (kl_out) kl_out[t] = l;
     }
   }
   __syncthreads();
@@ -239,14 +278,51 @@ __global__ void __launch_bounds__(256) merge_kernel(const float2* __restrict__ p
   }
 }
 
-// loss = (sum of block sums) / N, summed in a fixed order.
+// loss = (sum of block sums) / N, summed in a fixed order; with `count` (the
+// counted rows, from count_rows_kernel) the divisor is that count (loss 0 when
+// it is 0).
 __global__ void __launch_bounds__(256) loss_kernel(const double* __restrict__ block_sums, int nb, double inv_n,
-                                                   float* __restrict__ loss) {
+                                                   const double* __restrict__ count, float* __restrict__ loss) {
   __shared__ double sh[256];
   double a = 0.0;
   for (int b = threadIdx.x; b < nb; b += 256) a += block_sums[b];
   const double s = block_sum_256(a, sh);
-  if (threadIdx.x == 0) *loss = (float)(s * inv_n);
+  if (threadIdx.x == 0) {
+    const double inv = count ? (*count > 0.0 ? 1.0 / *count : 0.0) : inv_n;
+    *loss = (float)(s * inv);
+  }
+}
+
+// Number of rows whose label differs from `ignore` (one block, fixed order), and
+// the gradient scale g / count that the backward applies to every counted row
+// (0 when no row counts).
+__global__ void __launch_bounds__(1024) count_rows_kernel(const int32_t* __restrict__ labels, int64_t n,
+                                                          int ignore, const float* __restrict__ grad,
+                                                          double* __restrict__ count_out,
+                                                          float* __restrict__ scale_out) {
+  __shared__ long long sh[1024];
+  long long c = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) c += labels[i] != ignore;
+  sh[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const long long tot = sh[0];
+    *count_out = (double)tot;
+    if (scale_out) scale_out[0] = tot > 0 ? (grad ? *grad : 1.0f) * (1.0f / (float)tot) : 0.0f;
+  }
+}
+
+// lse of the counted rows, +inf for the ignored ones: the dZ epilogue's
+// exp(z - lse) is then exactly 0 on an ignored row.
+__global__ void __launch_bounds__(256) mask_lse_kernel(const float* __restrict__ lse,
+                                                       const int32_t* __restrict__ labels, int nr, int ignore,
+                                                       float* __restrict__ out) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < nr) out[t] = labels[t] != ignore ? lse[t] : INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -275,11 +351,15 @@ __global__ void __launch_bounds__(256) transpose_pad_kernel(const T* __restrict_
 // threads per row.  Entries are applied in batches of RB_TPR in k order: within a
 // batch, repeated indices are summed (in k order) by their first occurrence, and
 // a block barrier orders the batches, so every element is updated by one thread
-// at a time and repeated indices accumulate.
+// at a time and repeated indices accumulate.  With labels, rows whose label
+// equals `ignore` are left alone (their dZ row is 0 already), and with alpha > 0
+// the teacher is weighted by 1 - alpha and the label is one more entry (k = kc)
+// of weight alpha.
 template <typename T, typename VT>
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ idx, const VT* __restrict__ val,
                                                       int nr, int kc, int vocab, float inv_tau,
                                                       const float* __restrict__ grad, float inv_n,
+                                                      const int32_t* __restrict__ labels, int ignore, float alpha,
                                                       T* __restrict__ dz, int64_t ldz, T* __restrict__ dzt,
                                                       int64_t ldzt) {
   __shared__ float sh[4 * RB_ROWS];
@@ -287,26 +367,28 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
   __shared__ float bpe[RB_ROWS][RB_TPR];
   const int r = threadIdx.x & (RB_ROWS - 1), q = threadIdx.x / RB_ROWS;
   const int t = blockIdx.x * RB_ROWS + r;
-  const bool valid = t < nr;
+  const bool counted = t < nr && (labels == nullptr || labels[t] != ignore);
   const float scale = (grad ? *grad : 1.0f) * inv_n;
+  const float wt = scale * (1.0f - alpha);
+  const int ke = kc + (alpha > 0.f ? 1 : 0);
   const VT* vr = val + (int64_t)t * kc;
   const int32_t* ir = idx + (int64_t)t * kc;
   float vmax = -INFINITY;
-  if (valid)
+  if (counted)
     for (int k = q; k < kc; k += RB_TPR) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
   vmax = row_max(vmax, sh);
   float Z = 0.f;
-  if (valid)
+  if (counted)
     for (int k = q; k < kc; k += RB_TPR) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
   const float logZ = logf(row_sum(Z, sh));
-  for (int k0 = 0; k0 < kc; k0 += RB_TPR) {
+  for (int k0 = 0; k0 < ke; k0 += RB_TPR) {
     const int k = k0 + q;
     int v = -1;
     float pe = 0.f;
-    if (valid && k < kc) {
-      v = ir[k];
+    if (counted && k < ke) {
+      v = k < kc ? ir[k] : labels[t];
       if ((unsigned)v >= (unsigned)vocab) v = -1;
-      else pe = scale * expf(to_f32<VT>(vr[k]) * inv_tau - vmax - logZ);
+      else pe = k < kc ? wt * expf(to_f32<VT>(vr[k]) * inv_tau - vmax - logZ) : scale * alpha;
     }
     bidx[r][q] = v;
     bpe[r][q] = pe;

@@ -62,7 +62,8 @@ struct Plan {
 // Workspace regions, each 256-byte aligned, in bytes from the workspace start.
 struct Layout {
   size_t entries, offsets, zg, partials, block_sums, flags;       // forward
-  size_t wt, ht, dz, dzt, dhp;                                    // backward
+  size_t wt, ht, dz, dzt, dhp, lse_eff;                           // backward
+  size_t count;                                                   // counted rows (+ gradient scale)
   size_t s, bmax, wmax, overflow, tops, todo;                     // cache build
   size_t total;
 };
@@ -131,12 +132,14 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
   std::memset(L, 0, sizeof(*L));
   const int64_t n_tx = pl.Nc / BX;
   if (op == KD_OP_KL_FWD) {
-    L->entries = take(sizeof(uint32_t) * pl.Nc * pl.K);
+    // one more entry per row for a label (cross-entropy mix)
+    L->entries = take(sizeof(uint32_t) * pl.Nc * (pl.K + 1));
     L->offsets = take(sizeof(int) * n_tx * (pl.n_ty + 1));
-    L->zg = take(sizeof(float) * pl.Nc * pl.K);
+    L->zg = take(sizeof(float) * pl.Nc * (pl.K + 1));
     L->partials = take(sizeof(float2) * pl.n_ty * pl.Nc);
     L->block_sums = take(sizeof(double) * (size_t)std::max<int64_t>(1, cdiv(pl.N, RB_ROWS)));
     L->flags = take(sizeof(int) * 4);
+    L->count = take(16);
   } else if (op == KD_OP_KL_BWD) {
     if (!(pl.xdt == KD_BF16 && pl.N <= kWkmMaxTokens)) L->wt = take((size_t)(pl.esz * pl.d * pl.ld_v));
     L->ht = take((size_t)(pl.esz * pl.d * pl.ld_t));
@@ -151,6 +154,8 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     for (int64_t nr : {full, last})
       if (nr > 0 && dh_splits(pl, nr) > 1) part = std::max<int64_t>(part, dh_splits(pl, nr) * nr * pl.d);
     if (part) L->dhp = take((size_t)(4 * part));
+    L->lse_eff = take(sizeof(float) * (size_t)pl.Nc);
+    L->count = take(16);
   } else {
     L->s = take(sizeof(float) * (size_t)(pl.Nc * pl.ld_v));
     L->bmax = take(sizeof(double) * 1024);
@@ -283,9 +288,28 @@ kd_status zero_words(void* p, int64_t n_words, hipStream_t st) {
   });
 }
 
+// Loss variants (kd_loss_opts): labels (NULL = every row counts, no mix), the
+// label that marks an ignored row, and the cross-entropy weight.
+struct Opts {
+  const int32_t* labels = nullptr;
+  int ignore = 0;
+  float alpha = 0.f;
+};
+
+// Counted rows (double) and, with `scale`, g / count (float) into ws + L.count.
+kd_status count_rows(const Plan& pl, const Layout& L, const Opts& o, const float* grad, bool scale, char* ws,
+                     hipStream_t st) {
+  double* cnt = (double*)(ws + L.count);
+  float* gs = scale ? (float*)(ws + L.count + 8) : nullptr;
+  return launch("count", 0.0, 4.0 * pl.N, st, [&] {
+    hipLaunchKernelGGL(count_rows_kernel, dim3(1), dim3(1024), 0, st, o.labels, pl.N, o.ignore, grad, cnt, gs);
+  });
+}
+
 template <typename T>
 kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
-                   const void* val, float* loss, float* lse, float* kl_rows, char* ws, hipStream_t st) {
+                   const void* val, float* loss, float* lse, float* kl_rows, char* ws, hipStream_t st,
+                   const Opts& o) {
   uint32_t* entries = (uint32_t*)(ws + L.entries);
   int* offsets = (int*)(ws + L.offsets);
   float* zg = (float*)(ws + L.zg);
@@ -296,19 +320,23 @@ kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
   if (check) KD_TRY(zero_words(flags, 4, st));
   const float inv_tau = 1.0f / pl.tau;
   const int vsz = pl.vdt == KD_BF16 ? 2 : 4;
+  const int add_label = o.alpha > 0.f ? 1 : 0;
+  const int kz = pl.K + add_label;   // gathered logits per row: the K entries, then the label's
+  if (o.labels) KD_TRY(count_rows(pl, L, o, nullptr, false, ws, st));
   for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
     const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
     const int n_tx = (int)cdiv(nr, BX);
     const int32_t* idx_c = idx + r0 * pl.K;
+    const int32_t* lab_c = o.labels ? o.labels + r0 : nullptr;
     const size_t hist_bytes = sizeof(int) * (pl.n_ty + 64);
-    KD_TRY(launch("bucket", 0.0, 12.0 * nr * pl.K, st, [&] {
-      hipLaunchKernelGGL(bucket_kernel, dim3(n_tx), dim3(1024), hist_bytes, st, idx_c, nr, pl.K, (int)pl.V,
-                         pl.n_ty, entries, offsets, flags);
+    KD_TRY(launch("bucket", 0.0, 12.0 * nr * kz, st, [&] {
+      hipLaunchKernelGGL(bucket_kernel, dim3(n_tx), dim3(1024), hist_bytes, st, idx_c, lab_c, o.ignore, add_label,
+                         nr, pl.K, kz, (int)pl.V, pl.n_ty, entries, offsets, flags);
     }));
     GemmArgs g = gemm_args((const T*)h + r0 * pl.d, pl.d, nr, w, pl.d, (int)pl.V, (int)pl.d);
     g.entries = entries;
     g.offsets = offsets;
-    g.kc = pl.K;
+    g.kc = kz;
     g.zg = zg;
     g.partials = partials;
     g.ld_part = pl.Nc;
@@ -318,18 +346,18 @@ kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     KD_TRY(launch("merge", 0.0, mbytes, st, [&] {
       if (pl.vdt == KD_BF16)
         hipLaunchKernelGGL(merge_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty,
-                           idx_c, (const bf16_t*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
-                           kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / RB_ROWS);
+                           idx_c, (const bf16_t*)val + r0 * pl.K, zg, nr, pl.K, kz, (int)pl.V, inv_tau, lab_c,
+                           o.ignore, o.alpha, lse + r0, kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / RB_ROWS);
       else
         hipLaunchKernelGGL(merge_kernel<float>, dim3(nb), dim3(256), 0, st, partials, (int64_t)pl.Nc, pl.n_ty,
-                           idx_c, (const float*)val + r0 * pl.K, zg, nr, pl.K, (int)pl.V, inv_tau, lse + r0,
-                           kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / RB_ROWS);
+                           idx_c, (const float*)val + r0 * pl.K, zg, nr, pl.K, kz, (int)pl.V, inv_tau, lab_c,
+                           o.ignore, o.alpha, lse + r0, kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / RB_ROWS);
     }));
   }
   const int nb_all = (int)cdiv(pl.N, RB_ROWS);
   KD_TRY(launch("loss", 0.0, 8.0 * nb_all, st, [&] {
     hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsums, nb_all, pl.N > 0 ? 1.0 / (double)pl.N : 0.0,
-                       loss);
+                       o.labels ? (const double*)(ws + L.count) : nullptr, loss);
   }));
   if (check) {
     int bad = 0;
@@ -351,7 +379,7 @@ kd_status run_dh(const GemmArgs& g, bool w_kmajor, int64_t out_bytes, hipStream_
 template <typename T>
 kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
                    const void* val, const float* lse, const float* grad, void* dh, float* dw, char* ws,
-                   hipStream_t st) {
+                   hipStream_t st, const Opts& o) {
   if (pl.N == 0) return zero_words(dw, pl.V * pl.d, st);
   // W^T and H^T are cheap copies (W once, H per chunk).  dZ^T would cost a second
   // N x V write per chunk: bf16 reads dZ K-major in the dW product instead
@@ -361,9 +389,16 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
   T* ht = (T*)(ws + L.ht);
   T* dz = (T*)(ws + L.dz);
   T* dzt = kKm ? nullptr : (T*)(ws + L.dzt);
-  const float inv_n = 1.0f / (float)pl.N;
+  float inv_n = 1.0f / (float)pl.N;
   const float inv_tau = 1.0f / pl.tau;
   const int64_t es = (int64_t)sizeof(T);
+  float* lse_eff = (float*)(ws + L.lse_eff);
+  if (o.labels) {
+    // the scale g / (counted rows) is computed on the device and read in place of g
+    KD_TRY(count_rows(pl, L, o, grad, true, ws, st));
+    grad = (const float*)(ws + L.count + 8);
+    inv_n = 1.0f;
+  }
   const bool w_km = kKm && pl.N <= kWkmMaxTokens;
   if (!w_km) {
     // W^T [d][V_pad], zero past V
@@ -392,18 +427,25 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     g.lse = lse + r0;
     g.grad = grad;
     g.inv_n = inv_n;
+    if (o.labels) {
+      KD_TRY(launch("mask_lse", 0.0, 12.0 * nr, st, [&] {
+        hipLaunchKernelGGL(mask_lse_kernel, dim3((unsigned)cdiv(nr, 256)), dim3(256), 0, st, lse + r0,
+                           o.labels + r0, nr, o.ignore, lse_eff);
+      }));
+      g.lse = lse_eff;
+    }
     KD_TRY((run_gemm<T, EPI_KL_DZ>("gemm_dz", g, (kKm ? 1 : 2) * es * nr * pl.V, st)));
     // subtract the teacher at the cached entries
     const int nb = (int)cdiv(nr, RB_ROWS);
     KD_TRY(launch("scatter", 0.0, (double)nr * pl.K * (8.0 + (kKm ? 2.0 : 4.0) * es), st, [&] {
       if (pl.vdt == KD_BF16)
         hipLaunchKernelGGL((scatter_kernel<T, bf16_t>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
-                           (const bf16_t*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.ld_v,
-                           dzt, pl.ld_t);
+                           (const bf16_t*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n,
+                           o.labels ? o.labels + r0 : nullptr, o.ignore, o.alpha, dz, pl.ld_v, dzt, pl.ld_t);
       else
         hipLaunchKernelGGL((scatter_kernel<T, float>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
-                           (const float*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n, dz, pl.ld_v,
-                           dzt, pl.ld_t);
+                           (const float*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n,
+                           o.labels ? o.labels + r0 : nullptr, o.ignore, o.alpha, dz, pl.ld_v, dzt, pl.ld_t);
     }));
     // dH = dZ W  (P[t][j] = sum_v dZ[t][v] W^T[j][v], or W read K-major)
     GemmArgs gh = w_km ? gemm_args(dz, pl.ld_v, nr, w, pl.d, (int)pl.d, (int)pl.V_pad)
@@ -535,11 +577,33 @@ kd_status kd_topk_cache_build(const kd_problem* p, const void* h_t, const void* 
   return topk_impl<float, float>(pl, L, h_t, w_t, idx_out, val_out, (char*)ws, st);
 }
 
-kd_status kd_chunked_kl_fwd(const kd_problem* p, const void* h, const void* w, const int32_t* idx,
-                            const void* val, float* loss_out, float* lse_out, float* kl_rows_out, void* ws,
-                            size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Options of the _ex calls: NULL, or labels NULL with no mix, is the plain loss.
+kd_status read_opts(const kd_problem* p, const kd_loss_opts* opts, Opts* o) {
+  *o = Opts{};
+  if (!opts) return KD_OK;
+  if (!(std::isfinite(opts->ce_weight) && opts->ce_weight >= 0.f && opts->ce_weight <= 1.f))
+    return KD_ERR_BAD_OPTION;
+  if (!opts->labels) return opts->ce_weight > 0.f ? KD_ERR_BAD_OPTION : KD_OK;
+  if ((reinterpret_cast<uintptr_t>(opts->labels) & 3u) != 0) return KD_ERR_MISALIGNED;
+  if (p && p->n_tokens > 0) {
+    o->labels = opts->labels;
+    o->ignore = opts->ignore_index;
+    o->alpha = opts->ce_weight;
+  }
+  return KD_OK;
+}
+
+kd_status fwd_entry(const kd_problem* p, const kd_loss_opts* opts, const void* h, const void* w,
+                    const int32_t* idx, const void* val, float* loss_out, float* lse_out, float* kl_rows_out,
+                    void* ws, size_t ws_bytes, void* stream) {
   Plan pl;
   KD_TRY(validate(KD_OP_KL_FWD, p, &pl));
+  Opts o;
+  KD_TRY(read_opts(p, opts, &o));
   if (!w || !loss_out || !ws) return KD_ERR_NULL_POINTER;
   if (pl.N > 0 && (!h || !idx || !val || !lse_out)) return KD_ERR_NULL_POINTER;
   if (!aligned16(h) || !aligned16(w) || !aligned16(idx) || !aligned16(val) || !aligned16(loss_out) ||
@@ -550,15 +614,17 @@ kd_status kd_chunked_kl_fwd(const kd_problem* p, const void* h, const void* w, c
   KD_TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
   if (pl.xdt == KD_BF16)
-    return fwd_impl<bf16_t>(pl, L, h, w, idx, val, loss_out, lse_out, kl_rows_out, (char*)ws, st);
-  return fwd_impl<float>(pl, L, h, w, idx, val, loss_out, lse_out, kl_rows_out, (char*)ws, st);
+    return fwd_impl<bf16_t>(pl, L, h, w, idx, val, loss_out, lse_out, kl_rows_out, (char*)ws, st, o);
+  return fwd_impl<float>(pl, L, h, w, idx, val, loss_out, lse_out, kl_rows_out, (char*)ws, st, o);
 }
 
-kd_status kd_chunked_kl_bwd(const kd_problem* p, const void* h, const void* w, const int32_t* idx,
-                            const void* val, const float* lse, const float* grad_loss, void* dh_out, float* dw_out,
-                            void* ws, size_t ws_bytes, void* stream) {
+kd_status bwd_entry(const kd_problem* p, const kd_loss_opts* opts, const void* h, const void* w,
+                    const int32_t* idx, const void* val, const float* lse, const float* grad_loss, void* dh_out,
+                    float* dw_out, void* ws, size_t ws_bytes, void* stream) {
   Plan pl;
   KD_TRY(validate(KD_OP_KL_BWD, p, &pl));
+  Opts o;
+  KD_TRY(read_opts(p, opts, &o));
   if (!w || !dw_out || !ws) return KD_ERR_NULL_POINTER;
   if (pl.N > 0 && (!h || !idx || !val || !lse || !dh_out)) return KD_ERR_NULL_POINTER;
   if (!aligned16(h) || !aligned16(w) || !aligned16(idx) || !aligned16(val) || !aligned16(lse) ||
@@ -569,8 +635,36 @@ kd_status kd_chunked_kl_bwd(const kd_problem* p, const void* h, const void* w, c
   KD_TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
   if (pl.xdt == KD_BF16)
-    return bwd_impl<bf16_t>(pl, L, h, w, idx, val, lse, grad_loss, dh_out, dw_out, (char*)ws, st);
-  return bwd_impl<float>(pl, L, h, w, idx, val, lse, grad_loss, dh_out, dw_out, (char*)ws, st);
+    return bwd_impl<bf16_t>(pl, L, h, w, idx, val, lse, grad_loss, dh_out, dw_out, (char*)ws, st, o);
+  return bwd_impl<float>(pl, L, h, w, idx, val, lse, grad_loss, dh_out, dw_out, (char*)ws, st, o);
+}
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_chunked_kl_fwd(const kd_problem* p, const void* h, const void* w, const int32_t* idx,
+                            const void* val, float* loss_out, float* lse_out, float* kl_rows_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return fwd_entry(p, nullptr, h, w, idx, val, loss_out, lse_out, kl_rows_out, ws, ws_bytes, stream);
+}
+
+kd_status kd_chunked_kl_fwd_ex(const kd_problem* p, const kd_loss_opts* opts, const void* h, const void* w,
+                               const int32_t* idx, const void* val, float* loss_out, float* lse_out,
+                               float* rows_out, void* ws, size_t ws_bytes, void* stream) {
+  return fwd_entry(p, opts, h, w, idx, val, loss_out, lse_out, rows_out, ws, ws_bytes, stream);
+}
+
+kd_status kd_chunked_kl_bwd(const kd_problem* p, const void* h, const void* w, const int32_t* idx,
+                            const void* val, const float* lse, const float* grad_loss, void* dh_out, float* dw_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return bwd_entry(p, nullptr, h, w, idx, val, lse, grad_loss, dh_out, dw_out, ws, ws_bytes, stream);
+}
+
+kd_status kd_chunked_kl_bwd_ex(const kd_problem* p, const kd_loss_opts* opts, const void* h, const void* w,
+                               const int32_t* idx, const void* val, const float* lse, const float* grad_loss,
+                               void* dh_out, float* dw_out, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_entry(p, opts, h, w, idx, val, lse, grad_loss, dh_out, dw_out, ws, ws_bytes, stream);
 }
 
 const char* kd_status_string(kd_status s) {
@@ -585,15 +679,16 @@ const char* kd_status_string(kd_status s) {
     case KD_ERR_NO_DEVICE: return "no HIP device is current";
     case KD_ERR_UNSUPPORTED_ARCH: return "the current device is not gfx950 (MI355X)";
     case KD_ERR_LAUNCH: return "a kernel launch failed";
-    case KD_ERR_IDX_OUT_OF_RANGE: return "a cached index is outside [0, V)";
+    case KD_ERR_IDX_OUT_OF_RANGE: return "a cached index (or a mixed-in label) is outside [0, V)";
     case KD_ERR_TOPK_OVERFLOW: return "too many near-ties at the K-th teacher logit";
     case KD_ERR_IO: return "a cache file could not be opened, read or written";
     case KD_ERR_BAD_FORMAT: return "a cache shard does not match the shard format";
+    case KD_ERR_BAD_OPTION: return "a loss option is outside its domain";
   }
   return "unknown status";
 }
 
-int kd_version(void) { return 100; }
+int kd_version(void) { return 101; }
 
 kd_status kd_profile_begin(void) {
   Prof& p = prof();

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.kd_version() == 100
+    assert lib.kd_version() == 101
 
 
 def test_status_strings(lib):

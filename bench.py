@@ -207,6 +207,42 @@ def cache_io(kd, torch, idx, val, vocab, shards=4, batch=16384, prefetch=3):
         shutil.rmtree(d, ignore_errors=True)
 
 
+def variants(kd, torch, h, wd, idx, val, w, dh_dtype, steps, chunk, ce_weight=0.5, seq=32768, pad_frac=1 / 16):
+    """The same step with the loss options on: labels drawn over the vocabulary,
+    the last ``pad_frac`` of every ``seq``-token sequence marked as padding
+    (ignore index -100), and a cross-entropy mix of weight ``ce_weight``.  Tokens/s
+    counts every token of the batch, padded or not."""
+    n = h.shape[0]
+    g = torch.Generator().manual_seed(7)
+    lab = torch.randint(0, w.vocab, (n,), generator=g, dtype=torch.int32)
+    pos = torch.arange(n) % seq
+    lab[pos >= seq - int(seq * pad_frac)] = -100
+    ignored = float((lab == -100).float().mean())
+    lab = lab.to(h.device)
+
+    def vstep():
+        loss, lse, _ = kd.kd_chunked_kl_fwd(h, wd, idx, val, w.tau, chunk_tokens=chunk, labels=lab,
+                                            ce_weight=ce_weight)
+        dh, dw = kd.kd_chunked_kl_bwd(h, wd, idx, val, w.tau, lse, None, dh_dtype=dh_dtype, chunk_tokens=chunk,
+                                      labels=lab, ce_weight=ce_weight)
+        return loss, dh, dw
+
+    vstep()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out = None
+    for _ in range(steps):
+        out = None
+        out = vstep()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    loss = out[0].item()
+    del out
+    return {"tokens_per_s": n / (ms / 1e3), "ms_per_step": round(ms, 3), "ce_weight": ce_weight,
+            "ignored_frac": round(ignored, 4), "loss": round(loss, 5),
+            "options": f"labels over V, last 1/{round(1 / pad_frac)} of every {seq}-token sequence ignored"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +257,8 @@ def main() -> int:
     ap.add_argument("--no-cache-build-timing", action="store_true")
     ap.add_argument("--no-cache-io", action="store_true",
                     help="skip writing the cache to shards and streaming it back with the loader")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip timing the step with the loss options (padding mask, cross-entropy mix)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration) and exit")
     ap.add_argument("--sweep", action="store_true",
@@ -344,6 +382,12 @@ def main() -> int:
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom_kind), "kernel": dom_kind,
                 "avg_launch_ms": round(avg_s * 1e3, 4)}
 
+    var = None
+    if not args.no_variants:
+        var = variants(kd, torch, h, wd, idx, val, w, dh_dtype, max(1, min(args.steps, 3)), args.chunk)
+        log(f"loss options (mask {100 * var['ignored_frac']:.2f} % of tokens, CE weight {var['ce_weight']}): "
+            f"{var['ms_per_step']:.2f} ms/step, {var['tokens_per_s']:.0f} tokens/s")
+
     cio = None
     if not args.no_cache_io:
         cio = cache_io(kd, torch, idx, val, w.vocab)
@@ -365,7 +409,7 @@ def main() -> int:
         "config": {"workload": args.workload, "n_tokens": n, "d": w.d, "vocab": w.vocab, "k": k, "tau": w.tau,
                    "chunk_tokens": args.chunk or "default", "teacher": w.teacher},
         "mfma_util": round(mfma_util, 4), "peak_gb": round(peak_gb, 3),
-        "roofline": roof, "cpu_baseline": cpu, "cache_build": cache, "cache_io": cio,
+        "roofline": roof, "cpu_baseline": cpu, "cache_build": cache, "cache_io": cio, "loss_options": var,
         "kernels_ms_per_step": {k2: round(s["total_ms"] / args.steps, 4) for k2, s in stats.items()},
     }
     print(json.dumps(line), flush=True)

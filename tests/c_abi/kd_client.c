@@ -3,13 +3,17 @@
  * the HIP runtime's C API only.  It reads a problem file, builds the teacher's
  * top-K cache, runs the forward and the backward, and writes the results.  It
  * then writes the cache to two shard files in DIR (include/kdcache.h), streams them
- * back to the device with the loader and runs the forward again on that copy:
+ * back to the device with the loader and runs the forward again on that copy.
+ * Last, the loss options (kd_loss_opts): labels[i] = -100 (ignored) when
+ * i % 7 == 3, else (131 i) mod V, with a cross-entropy weight of 0.25, through the
+ * _ex forward and backward:
  *
  *   kd_client IN OUT DIR
  *   IN : int64 N, d, V; int32 K; float tau; then H [N*d], W [V*d], W_T [V*d] as bf16
  *        bits (uint16), teacher hidden states = H
  *   OUT: int32 status; then idx [N*K] int32, val [N*K] bf16 bits, loss float,
- *        lse [N] float, dH [N*d] float, dW [V*d] float, loss from the reloaded cache float
+ *        lse [N] float, dH [N*d] float, dW [V*d] float, loss from the reloaded cache float,
+ *        then with the options: loss float, dH [N*d] float, dW [V*d] float
  *
  * Exit status 0 on success; on a library error the kd_status is printed with
  * kd_status_string() and the exit status is 1.
@@ -144,12 +148,34 @@ int main(int argc, char** argv) {
   float loss2 = 0.f;
   HIP_OK(hipMemcpy(&loss2, dloss2, 4, hipMemcpyDeviceToHost));
 
+  /* the loss options: a padding mask and a hard-label mix */
+  int32_t* lab = malloc(4 * (size_t)N + 4);
+  if (!lab) return 2;
+  for (int64_t i = 0; i < N; ++i) lab[i] = (i % 7 == 3) ? -100 : (int32_t)((131 * i) % V);
+  void* dlab;
+  HIP_OK(hipMalloc(&dlab, 4 * (size_t)N + 16));
+  HIP_OK(hipMemcpy(dlab, lab, 4 * (size_t)N, hipMemcpyHostToDevice));
+  const kd_loss_opts opts = {(const int32_t*)dlab, -100, 0.25f};
+  KD_OK_OR_FAIL(kd_chunked_kl_fwd_ex(&p, &opts, dh_in, dw_in, (const int32_t*)didx, dval, (float*)dloss2,
+                                     (float*)dlse, NULL, dws, ws_bytes, st));
+  KD_OK_OR_FAIL(kd_chunked_kl_bwd_ex(&p, &opts, dh_in, dw_in, (const int32_t*)didx, dval, (const float*)dlse, NULL,
+                                     ddh, (float*)ddw, dws, ws_bytes, st));
+  HIP_OK(hipStreamSynchronize(st));
+  float loss3 = 0.f;
+  float* dhh3 = malloc(4 * nh + 4);
+  float* dwh3 = malloc(4 * nw);
+  if (!dhh3 || !dwh3) return 2;
+  HIP_OK(hipMemcpy(&loss3, dloss2, 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(dhh3, ddh, 4 * nh, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(dwh3, ddw, 4 * nw, hipMemcpyDeviceToHost));
+
   FILE* fo = fopen(argv[2], "wb");
   if (!fo) return 2;
   const int32_t ok = 0;
   if (!write_all(fo, &ok, 4) || !write_all(fo, idx, 4 * nk) || !write_all(fo, val, 2 * nk) ||
       !write_all(fo, &loss, 4) || !write_all(fo, lse, 4 * (size_t)N) || !write_all(fo, dhh, 4 * nh) ||
-      !write_all(fo, dwh, 4 * nw) || !write_all(fo, &loss2, 4))
+      !write_all(fo, dwh, 4 * nw) || !write_all(fo, &loss2, 4) || !write_all(fo, &loss3, 4) ||
+      !write_all(fo, dhh3, 4 * nh) || !write_all(fo, dwh3, 4 * nw))
     return 2;
   fclose(fo);
   printf("kd_client: N=%lld d=%lld V=%lld K=%d loss=%.6f (kd_version %d)\n", (long long)N, (long long)d,

@@ -3,7 +3,8 @@ with gcc against libkdkl.so and the HIP runtime's C API, no torch) builds the
 teacher cache, runs the forward and the backward; its outputs must match the
 float64 oracle on the same inputs.  It also writes the cache to shard files and
 streams them back with the loader (include/kdcache.h): the loss from that copy must
-be the same float."""
+be the same float.  Last it runs the _ex calls with a padding mask and a hard-label
+mix (kd_loss_opts), checked against ``oracle.variant_forward`` / ``variant_backward``."""
 import os
 import subprocess
 
@@ -50,6 +51,9 @@ def test_c_client_matches_oracle(tmp_path):
     g_dh = take(np.float32, n * d).reshape(n, d)
     g_dw = take(np.float32, v * d).reshape(v, d)
     g_loss2 = take(np.float32, 1)[0]
+    g_loss3 = float(take(np.float32, 1)[0])
+    g_dh3 = take(np.float32, n * d).reshape(n, d)
+    g_dw3 = take(np.float32, v * d).reshape(v, d)
     assert off == len(buf)
     assert np.float32(g_loss) == g_loss2                 # same cache bytes, same loss
     assert (tmp_path / "c0.kdc").exists() and (tmp_path / "c1.kdc").exists()
@@ -67,3 +71,12 @@ def test_c_client_matches_oracle(tmp_path):
     np.testing.assert_allclose(g_lse.astype(np.float64), ref_lse, rtol=LSE_RTOL)
     assert rel_max_err(g_dh.astype(np.float64), ref_dH) <= GRAD_TOL
     assert rel_max_err(g_dw.astype(np.float64), ref_dW) <= GRAD_TOL
+
+    i = np.arange(n)
+    labels = np.where(i % 7 == 3, -100, (131 * i) % v).astype(np.int32)
+    ref_loss3, _, _ = oracle.variant_forward(H, W, idx, v64, tau, labels, -100, 0.25)
+    ref_dH3, ref_dW3 = oracle.variant_backward(H, W, idx, v64, tau, labels, -100, 0.25)
+    assert abs(g_loss3 - ref_loss3) <= LOSS_RTOL * abs(ref_loss3)
+    assert rel_max_err(g_dh3.astype(np.float64), ref_dH3) <= GRAD_TOL
+    assert rel_max_err(g_dw3.astype(np.float64), ref_dW3) <= GRAD_TOL
+    assert not g_dh3[i % 7 == 3].any()

@@ -166,3 +166,50 @@ def test_peak_memory_linear_in_tokens():
     assert resid < 0.02
     assert b < 0.1 * 2 * w.vocab      # no N x V term
     assert b > 2 * w.d                 # at least H itself
+
+
+def test_loss_options_ctx32k_v128k():
+    """The loss options at full size, in the benchmark's launch configuration:
+    32,768 tokens, V = 128,256, d = 4,096, a synthetic cache of K = 100, labels
+    over the vocabulary with the last 1/16 of each 8,192 tokens ignored (padding)
+    and a cross-entropy weight of 0.5.  Sampled rows against the oracle (row
+    terms, lse, dH rows); the loss is the mean of the row terms over the counted
+    rows; dW's columns sum to zero (each counted dZ row still sums to zero)."""
+    w = kd_synth.WORKLOADS["ctx32k_v128k"]
+    n, k, a, ign = 32768, 100, 0.5, -100
+    print(f"[fullsize] loss options {w.name} N={n} K={k} a={a}", flush=True)
+    H = kd_synth.hidden(w, n)
+    W = kd_synth.student_head(w)
+    idx, valb = kd_synth.random_cache(n, w.vocab, k, seed=41)
+    g = np.random.default_rng(42)
+    labels = g.integers(0, w.vocab, size=n).astype(np.int32)
+    labels[np.arange(n) % 8192 >= 8192 - 512] = ign
+    h, wd = to_dev(H, w.dtype), to_dev(W, w.dtype)
+    ti, tv, tl = torch.from_numpy(idx).to(device()), to_dev(valb, "bf16"), torch.from_numpy(labels).to(device())
+    loss, lse, rows = kd.kd_chunked_kl_fwd(h, wd, ti, tv, w.tau, with_rows=True, labels=tl, ce_weight=a)
+    dh, dw = kd.kd_chunked_kl_bwd(h, wd, ti, tv, w.tau, lse, None, dh_dtype=torch.float32, labels=tl, ce_weight=a)
+    torch.cuda.synchronize()
+
+    count = int((labels != ign).sum())
+    rs = np.unique(np.concatenate([sample_rows(n, 20, seed=43), [8192 - 1, 8192 - 512, 8192 - 513]]))
+    rs_t = torch.from_numpy(rs).to(device())
+    H64 = kd_synth.to_float64(H[rs], w.dtype)
+    W64 = kd_synth.to_float64(W, w.dtype)
+    v64 = kd_synth.to_float64(valb[rs], "bf16")
+    _, ref_lse, ref_rows = oracle.variant_forward(H64, W64, idx[rs], v64, w.tau, labels[rs], ign, a)
+    np.testing.assert_allclose(to_f64(lse[rs_t]), ref_lse, rtol=LSE_RTOL)
+    np.testing.assert_allclose(to_f64(rows[rs_t]), ref_rows, rtol=LOSS_RTOL, atol=LOSS_RTOL)
+    # dH rows: the oracle divides by the sample's counted rows; rescale to the batch's
+    c_s = int((labels[rs] != ign).sum())
+    ref_dH, _ = oracle.variant_backward(H64, W64, idx[rs], v64, w.tau, labels[rs], ign, a)
+    ref_dH *= c_s / count
+    assert rel_max_err(to_f64(dh[rs_t]), ref_dH) <= GRAD_TOL
+    assert not dh[torch.from_numpy(labels == ign).to(device())].any()
+
+    r_all = rows.double()
+    assert torch.isfinite(r_all).all()
+    assert abs(r_all.sum().item() / count - loss.item()) <= 1e-5 * abs(loss.item())
+    dw64 = dw.double()
+    colsum = dw64.sum(0).abs()
+    bound = 2.0 ** -7 / count * h.double().abs().sum(0) * 1.01 + 2.0 ** -20 * dw64.abs().sum(0)
+    assert bool((colsum <= bound).all()), float((colsum / bound).max())

@@ -53,7 +53,7 @@
  *     come from the device check that follows validation; KD_ERR_LAUNCH reports a
  *     failed kernel launch. Asynchronous device faults surface at the caller's next
  *     synchronisation. The library never aborts, prints or throws.
- *   - Shape domain: N >= 0, d >= 8 with d % 8 == 0, 1 <= V <= 4194304,
+ *   - Shape domain: N >= 0, d >= 8 with d % 8 == 0, 1 <= V <= 2097088 (2^21 - 64),
  *     1 <= K <= min(V, 65535) (the cache build: K <= 4096), tau finite and > 0.
  *   - Cached indices must lie in [0, V). An out-of-range index is skipped by the
  *     kernels (no out-of-bounds access); it makes that row's KL NaN, and when the

@@ -20,7 +20,11 @@ using namespace kd;
 
 namespace {
 
-constexpr int64_t kMaxVocab = 4194304;   // 16384 vocabulary tiles (bucket histogram in LDS)
+// 2^21 - 64: the 256-row tiles of the operands with V-element rows (dZ, W^T; 4-byte
+// elements in the float32 path, padded by pad_ld) then span less than 2^31 bytes, so
+// the loads' out-of-range offset 0x80000000 stays past every tile's descriptor (the
+// 32-bit offset check in validate() below).  8,192 vocabulary tiles.
+constexpr int64_t kMaxVocab = 2097088;
 constexpr int kMaxK = 65535;             // k fits the 16-bit field of a bucket entry
 constexpr int kMaxKTopk = 4096;          // selection candidates are held in LDS
 constexpr int64_t kDefaultChunkKL = 16384;

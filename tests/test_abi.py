@@ -67,7 +67,7 @@ def _ws(lib, op, prob):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(d=0), 2), (dict(d=12), 2), (dict(v=0), 2), (dict(k=0), 2), (dict(k=1001), 2), (dict(n=-1), 2),
-    (dict(v=4194305, k=1), 2), (dict(k=70000, v=100000), 2), (dict(chunk_tokens=-5), 2),
+    (dict(v=2097089, k=1), 2), (dict(k=70000, v=100000), 2), (dict(chunk_tokens=-5), 2),
     (dict(tau=0.0), 4), (dict(tau=-1.0), 4), (dict(tau=float("nan")), 4), (dict(tau=float("inf")), 4),
     (dict(x_dtype=7), 3), (dict(val_dtype=kd.KD_F32), 3), (dict(x_dtype=kd.KD_F32, val_dtype=kd.KD_BF16), 3),
 ])
@@ -75,6 +75,18 @@ def test_workspace_size_rejects_bad_problems(lib, kw, status):
     for op in (kd.KD_OP_KL_FWD, kd.KD_OP_KL_BWD):
         st, _ = _ws(lib, op, _P(**kw))
         assert st == status, (kw, op, st)
+
+
+@pytest.mark.parametrize("x_dtype", [kd.KD_BF16, kd.KD_F32])
+def test_domain_limits_are_exact(lib, x_dtype):
+    """The header's largest V (2,097,088) and K (65,535; 4,096 for the cache build)
+    are accepted by every call and one more is refused."""
+    for op in (kd.KD_OP_TOPK_BUILD, kd.KD_OP_KL_FWD, kd.KD_OP_KL_BWD):
+        assert _ws(lib, op, _P(v=2097088, x_dtype=x_dtype))[0] == 0, op
+        assert _ws(lib, op, _P(v=2097089, x_dtype=x_dtype))[0] == 2, op
+        kmax = 4096 if op == kd.KD_OP_TOPK_BUILD else 65535
+        assert _ws(lib, op, _P(v=70000, k=kmax, x_dtype=x_dtype))[0] == 0, op
+        assert _ws(lib, op, _P(v=70000, k=kmax + 1, x_dtype=x_dtype))[0] == 2, op
 
 
 def test_workspace_size_null_and_bad_op(lib):

@@ -302,3 +302,32 @@ sys.exit(3)
     r = subprocess.run([sys.executable, "-c", script], env=env, cwd=root, stdout=subprocess.PIPE,
                        stderr=subprocess.STDOUT, text=True, timeout=180)
     assert r.returncode == 0 and "status 10" in r.stdout, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("tau", [0.02, 1e4])
+def test_teacher_temperature_extremes(tau):
+    """tau = 0.02 on cached logits spread over [-60, 60]: val / tau spans 6,000, so
+    all but the top entries' probabilities underflow to 0 in float32 (p log p is
+    taken as 0 there, and they leave the gradient); tau = 1e4: a near-uniform
+    teacher over the K entries."""
+    n, d, v, k = 300, 64, 1000, 24
+    print(f"[case] tau={tau}", flush=True)
+    p = kd_synth.small_problem(n, d, v, seed=71)
+    H = kd_synth.to_float64(p["H"], "bf16")
+    W = kd_synth.to_float64(p["W"], "bf16")
+    idx, _ = kd_synth.random_cache(n, v, k, seed=72)
+    g = np.random.default_rng(73)
+    valb = kd_synth.bf16_bits_from_f32(g.uniform(-60, 60, size=(n, k)).astype(np.float32))
+    val = kd_synth.to_float64(valb, "bf16")
+    ref_loss, ref_lse, ref_rows = oracle.kl_forward(H, W, idx, val, tau)
+    ref_dH, ref_dW = oracle.kl_backward(H, W, idx, val, tau)
+    h, w = to_dev(p["H"], "bf16"), to_dev(p["W"], "bf16")
+    ti, tv = torch.from_numpy(idx).to(device()), to_dev(valb, "bf16")
+    loss, lse, rows = kd.kd_chunked_kl_fwd(h, w, ti, tv, tau, with_rows=True)
+    dh, dw = kd.kd_chunked_kl_bwd(h, w, ti, tv, tau, lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(rows).all()
+    assert abs(loss.item() - ref_loss) <= LOSS_RTOL * abs(ref_loss)
+    np.testing.assert_allclose(to_f64(rows), ref_rows, rtol=5e-3, atol=5e-3)
+    assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL
+    assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL

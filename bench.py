@@ -268,8 +268,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the loss would shard over tokens with one dW all-reduce; see the design notes).",
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path (the loss "
+              "would shard over tokens, each GPU holding W, with one all-reduce of dW).",
               file=sys.stderr)
         return 2
 

@@ -16,7 +16,9 @@ Entry points (same names as the C ABI):
   mask and a hard-label cross-entropy mix), which select the C calls
   ``kd_chunked_kl_fwd_ex`` / ``kd_chunked_kl_bwd_ex``.
 * :class:`KDChunkedKL` / :func:`chunked_kl_loss` -- autograd wrapper (forward
-  saves ``lse``; backward calls :func:`kd_chunked_kl_bwd`).
+  saves ``lse``; backward calls :func:`kd_chunked_kl_bwd`);
+  :class:`ChunkedTopKKLLoss` -- the same as a ``torch.nn.Module`` over
+  ``[..., d]`` hidden states and ``[..., K]`` caches.
 * :func:`kd_cache_write`, :func:`kd_cache_info_read`, :func:`kd_cache_read` --
   on-disk cache shards (C ABI in ``include/kdcache.h``);
   :func:`kd_cache_loader_open` / :func:`kd_cache_loader_next` /
@@ -355,6 +357,42 @@ def chunked_kl_loss(h, w, idx, val, tau: float = 1.0, chunk_tokens: int = 0, lab
     with the labels."""
     return KDChunkedKL.apply(h, w, idx, val, float(tau), int(chunk_tokens), labels, int(ignore_index),
                              float(ce_weight))
+
+
+class ChunkedTopKKLLoss(torch.nn.Module):
+    """Drop-in loss module: ``loss = ChunkedTopKKLLoss(tau)(hidden, head_weight,
+    idx, val[, labels])``.
+
+    ``hidden`` is ``[..., d]`` (for example ``[batch, seq, d]``), ``idx`` / ``val``
+    are ``[..., K]`` and ``labels`` ``[...]`` over the same leading axes; they are
+    flattened to rows as views (no copy, so they must be contiguous).  The head
+    weight is ``[V, d]`` as in ``nn.Linear(d, V, bias=False).weight``.  Returns the
+    mean top-K KL over the tokens (over the counted tokens with labels), mixed with
+    the labels' cross-entropy when ``ce_weight`` > 0."""
+
+    def __init__(self, tau: float = 1.0, ignore_index: int = -100, ce_weight: float = 0.0,
+                 chunk_tokens: int = 0):
+        super().__init__()
+        self.tau = float(tau)
+        self.ignore_index = int(ignore_index)
+        self.ce_weight = float(ce_weight)
+        self.chunk_tokens = int(chunk_tokens)
+
+    def forward(self, hidden, weight, idx, val, labels=None):
+        d = hidden.shape[-1]
+        k = idx.shape[-1]
+        if idx.shape[:-1] != hidden.shape[:-1] or val.shape != idx.shape:
+            raise ValueError("idx / val must be [..., K] over the hidden states' leading axes")
+        if labels is not None and labels.shape != hidden.shape[:-1]:
+            raise ValueError("labels must have the hidden states' leading axes")
+        h = hidden.view(-1, d)
+        lab = None if labels is None else labels.view(-1)
+        return chunked_kl_loss(h, weight, idx.view(-1, k), val.view(-1, k), self.tau, self.chunk_tokens, lab,
+                               self.ignore_index, self.ce_weight)
+
+    def extra_repr(self) -> str:
+        return (f"tau={self.tau}, ignore_index={self.ignore_index}, ce_weight={self.ce_weight}, "
+                f"chunk_tokens={self.chunk_tokens}")
 
 
 # ---- on-disk cache shards and the streaming loader (include/kdcache.h)

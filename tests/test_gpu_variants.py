@@ -207,3 +207,24 @@ sys.exit(3)
     r = subprocess.run([sys.executable, "-c", script], env=env, cwd=root, stdout=subprocess.PIPE,
                        stderr=subprocess.STDOUT, text=True, timeout=180)
     assert r.returncode == 0 and "status 10" in r.stdout, r.stdout[-2000:]
+
+
+def test_loss_module_over_batch_and_sequence_axes():
+    """ChunkedTopKKLLoss on [batch, seq, d] hidden states and [batch, seq, K]
+    caches equals chunked_kl_loss on the flattened rows, loss and gradients."""
+    b, t, d, v, k = 3, 170, 64, 900, 8
+    p, vdt, idx, valb, labels = _inputs(b * t, d, v, k, "bf16", seed=31)
+    h, w, ti, tv, tl = _gpu(p, "bf16", idx, valb, labels, vdt)
+    mod = kd.ChunkedTopKKLLoss(tau=1.5, ce_weight=0.2)
+    h3 = h.view(b, t, d).clone().requires_grad_()
+    w1 = w.clone().requires_grad_()
+    loss = mod(h3, w1, ti.view(b, t, k), tv.view(b, t, k), tl.view(b, t))
+    loss.backward()
+    h2, w2 = h.clone().requires_grad_(), w.clone().requires_grad_()
+    ref = kd.chunked_kl_loss(h2, w2, ti, tv, 1.5, labels=tl, ce_weight=0.2)
+    ref.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(loss, ref)
+    assert torch.equal(h3.grad.view(-1, d), h2.grad) and torch.equal(w1.grad, w2.grad)
+    with pytest.raises(ValueError):
+        mod(h3, w1, ti, tv)

@@ -331,3 +331,29 @@ def test_teacher_temperature_extremes(tau):
     np.testing.assert_allclose(to_f64(rows), ref_rows, rtol=5e-3, atol=5e-3)
     assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL
     assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_exact_ties_take_the_smaller_index(dtype):
+    """Every teacher row appears twice (row v + 1,500 = row v), so every logit of a
+    row is tied with exactly one other and, with K = 51 odd, the K-th and K+1-th
+    entries are always a tied pair: the cache must keep the smaller index and order
+    each pair smaller index first, bit-exact with the oracle."""
+    n, d, v, k = 200, 64, 3000, 51
+    print(f"[case] ties {dtype}", flush=True)
+    p = kd_synth.small_problem(n, d, v, seed=81, dtype=dtype)
+    WT = p["WT"].copy()
+    WT[1500:] = WT[:1500]
+    ref_idx, ref_val, _ = oracle.topk_cache(kd_synth.to_float64(p["H"], dtype), kd_synth.to_float64(WT, dtype), k,
+                                            "bf16" if dtype == "bf16" else "f32")
+    gi, gv = kd.kd_topk_cache_build(to_dev(p["H"], dtype), to_dev(WT, dtype), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gi.cpu().numpy(), ref_idx)
+    if dtype == "bf16":
+        np.testing.assert_array_equal(bf16_bits_of(gv), ref_val)
+    else:
+        np.testing.assert_array_equal(gv.cpu().numpy().view(np.uint32), ref_val.view(np.uint32))
+    # the pairs: positions 2i and 2i+1 hold v and v + 1,500 (same value), the last
+    # position the smaller of its pair
+    gi_np = gi.cpu().numpy()
+    assert (gi_np[:, 0:50:2] + 1500 == gi_np[:, 1:50:2]).all() and (gi_np[:, 50] < 1500).all()

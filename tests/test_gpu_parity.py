@@ -357,3 +357,32 @@ def test_topk_exact_ties_take_the_smaller_index(dtype):
     # position the smaller of its pair
     gi_np = gi.cpu().numpy()
     assert (gi_np[:, 0:50:2] + 1500 == gi_np[:, 1:50:2]).all() and (gi_np[:, 50] < 1500).all()
+
+
+def test_uninformed_student_closed_form():
+    """W = 0: every student logit is 0, so lse = log V exactly, KL_i = sum_k p log p +
+    log V (a closed form, no oracle needed), dH = dZ W = 0 exactly and dW = dZ^T H
+    with dZ = (1/V - scatter(p)) / N."""
+    n, d, v, k, tau = 300, 64, 1000, 12, 1.7
+    print("[case] W = 0", flush=True)
+    p = kd_synth.small_problem(n, d, v, seed=91)
+    idx, valb = kd_synth.random_cache(n, v, k, seed=92)
+    val = kd_synth.to_float64(valb, "bf16")
+    pt = np.exp(val / tau - (val / tau).max(axis=1, keepdims=True))
+    pt /= pt.sum(axis=1, keepdims=True)
+    kl_rows = (np.where(pt > 0, pt * np.log(pt), 0.0)).sum(axis=1) + np.log(v)
+    H = kd_synth.to_float64(p["H"], "bf16")
+    dz = np.full((n, v), 1.0 / v)
+    np.add.at(dz, (np.repeat(np.arange(n), k), idx.ravel()), -pt.ravel())
+    ref_dW = (dz / n).T @ H
+    h = to_dev(p["H"], "bf16")
+    w = torch.zeros((v, d), dtype=torch.bfloat16, device=device())
+    ti, tv = torch.from_numpy(idx).to(device()), to_dev(valb, "bf16")
+    loss, lse, rows = kd.kd_chunked_kl_fwd(h, w, ti, tv, tau, with_rows=True)
+    dh, dw = kd.kd_chunked_kl_bwd(h, w, ti, tv, tau, lse)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_f64(lse), np.log(v), rtol=1e-6)
+    np.testing.assert_allclose(to_f64(rows), kl_rows, rtol=1e-4, atol=1e-5)
+    assert abs(loss.item() - kl_rows.mean()) <= LOSS_RTOL * abs(kl_rows.mean())
+    assert not dh.any()
+    assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL

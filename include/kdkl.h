@@ -122,6 +122,10 @@ kd_status kd_workspace_size(kd_op op, const kd_problem* p, size_t* bytes);
  *   h_t   [N, d] x_dtype          w_t [V, d] x_dtype
  *   idx_out [N, K] int32          val_out [N, K] val_dtype: the exact logit rounded
  *                                 once (nearest, ties to even) to bf16 / f32.
+ * A row with more than 6,144 logits within the error bound of its K-th value (a
+ * massive near-tie, e.g. thousands of identical teacher rows at the top) exceeds
+ * the candidate buffer: its idx are written as -1 and its val as NaN, and with
+ * KD_CHECK=1 the call synchronises and returns KD_ERR_TOPK_OVERFLOW.
  * tau and dh_dtype are ignored. */
 kd_status kd_topk_cache_build(const kd_problem* p, const void* h_t, const void* w_t,
                               int32_t* idx_out, void* val_out,

@@ -386,3 +386,60 @@ def test_uninformed_student_closed_form():
     assert abs(loss.item() - kl_rows.mean()) <= LOSS_RTOL * abs(kl_rows.mean())
     assert not dh.any()
     assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+
+
+def _overflow_problem():
+    """Rows 0-2: 7,000 identical teacher rows hold every top-K logit of the row, so
+    7,000 candidates lie within the error bound of the K-th value (more than the
+    6,144 the selection holds).  Row 3: the tied logits at the bottom, an ordinary
+    top-K from the other rows."""
+    n, d, v, k = 4, 64, 8000, 10
+    g = np.random.default_rng(95)
+    u = g.standard_normal(d).astype(np.float32) / 8
+    WT = (g.standard_normal((v, d)) * 0.01).astype(np.float32)
+    WT[:7000] = u
+    H = np.empty((n, d), dtype=np.float32)
+    H[:3] = u * 40
+    H[3] = -u * 40 + g.standard_normal(d).astype(np.float32)   # the tied rows sink to the bottom
+    return kd_synth.bf16_bits_from_f32(H), kd_synth.bf16_bits_from_f32(WT), k
+
+
+def test_topk_candidate_overflow_marks_the_row():
+    Hb, WTb, k = _overflow_problem()
+    print("[case] top-K candidate overflow", flush=True)
+    gi, gv = kd.kd_topk_cache_build(to_dev(Hb, "bf16"), to_dev(WTb, "bf16"), k)
+    torch.cuda.synchronize()
+    gi, gvf = gi.cpu().numpy(), gv.float().cpu().numpy()
+    assert (gi[:3] == -1).all() and np.isnan(gvf[:3]).all()
+    ref_idx, ref_val, _ = oracle.topk_cache(kd_synth.to_float64(Hb[3:], "bf16"), kd_synth.to_float64(WTb, "bf16"),
+                                            k, "bf16")
+    np.testing.assert_array_equal(gi[3:], ref_idx)
+    np.testing.assert_array_equal(bf16_bits_of(gv[3:]), ref_val)
+
+
+def test_kd_check_reports_topk_overflow():
+    """KD_CHECK=1 (read once per process, hence a child process): the cache build
+    synchronises and returns KD_ERR_TOPK_OVERFLOW for the overflowing rows."""
+    import subprocess
+    import sys
+    script = r'''
+import sys
+sys.path.insert(0, "tests")
+import numpy as np, torch
+import lm_head_kl_amd as kd
+from test_gpu_parity import _overflow_problem
+from gpu_util import to_dev
+Hb, WTb, k = _overflow_problem()
+try:
+    kd.kd_topk_cache_build(to_dev(Hb, "bf16"), to_dev(WTb, "bf16"), k)
+except kd.KDError as e:
+    assert e.status == 11, e.status
+    print("status", e.status)
+    sys.exit(0)
+sys.exit(3)
+'''
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, KD_CHECK="1", PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-c", script], env=env, cwd=root, stdout=subprocess.PIPE,
+                       stderr=subprocess.STDOUT, text=True, timeout=180)
+    assert r.returncode == 0 and "status 11" in r.stdout, r.stdout[-2000:]

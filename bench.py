@@ -207,6 +207,42 @@ def cache_io(kd, torch, idx, val, vocab, shards=4, batch=16384, prefetch=3):
         shutil.rmtree(d, ignore_errors=True)
 
 
+def cache_pipeline(kd, torch, h, wt, k, vocab, ref_idx, ref_val, batch=32768, shard=32768):
+    """The offline pass end to end: the teacher cache built batch by batch on the
+    GPU and handed to the streaming writer as it is produced, until every shard is
+    on disk (page cache).  Checks the shards against the cache built in one call.
+    Reports the writer's fixed costs (opening: pinned buffers; closing: the last
+    shard's write after the GPU is done) beside the whole."""
+    import shutil
+    import tempfile
+    n = h.shape[0]
+    d = tempfile.mkdtemp(prefix="kdpipe_")
+    try:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        wr = kd.CacheWriter(os.path.join(d, "cache"), shard, vocab, k, ref_val.dtype, batch)
+        t1 = time.perf_counter()
+        for r0 in range(0, n, batch):
+            i, v = kd.kd_topk_cache_build(h[r0:r0 + batch], wt, k)
+            wr.put(i, v)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        wr.close()
+        t3 = time.perf_counter()
+        got_i = torch.cat([kd.kd_cache_read(p)[0] for p in wr.paths])
+        got_v = torch.cat([kd.kd_cache_read(p)[1] for p in wr.paths])
+        bits = torch.int16 if got_v.dtype == torch.bfloat16 else torch.int32
+        if not (torch.equal(got_i, ref_idx.cpu()) and torch.equal(got_v.view(bits), ref_val.cpu().view(bits))):
+            raise RuntimeError("shards written by the pipeline differ from the cache built in one call")
+        t = t3 - t0
+        return {"tokens_per_s": n / t, "ms": round(t * 1e3, 1), "batch_tokens": batch, "shard_tokens": shard,
+                "shards": len(wr.paths), "bytes": sum(os.path.getsize(p) for p in wr.paths), "exact": True,
+                "open_ms": round((t1 - t0) * 1e3, 1), "gpu_ms": round((t2 - t1) * 1e3, 1),
+                "close_ms": round((t3 - t2) * 1e3, 1)}
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+
+
 def variants(kd, torch, h, wd, idx, val, w, dh_dtype, steps, chunk, ce_weight=0.5, seq=32768, pad_frac=1 / 16):
     """The same step with the loss options on: labels drawn over the vocabulary,
     the last ``pad_frac`` of every ``seq``-token sequence marked as padding
@@ -393,6 +429,14 @@ def main() -> int:
         cio = cache_io(kd, torch, idx, val, w.vocab)
         log(f"cache io: {cio['bytes'] / 1e6:.1f} MB in {cio['shards']} shards; write {cio['write_gbs']:.2f} GB/s, "
             f"loader to device {cio['load_gbs']:.2f} GB/s = {cio['load_tokens_per_s']:.0f} tokens/s")
+        wt = to_dev(kd_synth.teacher_head(w))
+        cio["pipeline"] = cache_pipeline(kd, torch, h, wt, k, w.vocab, idx, val)
+        del wt
+        torch.cuda.empty_cache()
+        cp = cio["pipeline"]
+        log(f"cache build + streaming writer: {cp['ms']:.1f} ms = {cp['tokens_per_s']:.0f} tokens/s "
+            f"(open {cp['open_ms']:.1f} ms, build and copies {cp['gpu_ms']:.1f} ms, last shard {cp['close_ms']:.1f} ms), "
+            f"{cp['shards']} shards, {cp['bytes'] / 1e6:.1f} MB")
 
     cpu = None
     if not args.no_cpu_baseline:

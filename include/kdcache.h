@@ -1,6 +1,7 @@
 /*
- * kdcache.h - C ABI of the on-disk teacher cache and its streaming loader: the
- * storage side of offline top-K distillation, next to the loss in kdkl.h.
+ * kdcache.h - C ABI of the on-disk teacher cache, its streaming writer and its
+ * streaming loader: the storage side of offline top-K distillation, next to the
+ * loss in kdkl.h.
  *
  * Sources (web pages about arXiv 2608.03796):
  *   [wiki] llm-wiki study note "LLM 지식 증류 효율화 ...":
@@ -103,6 +104,40 @@ kd_status kd_cache_loader_next(kd_cache_loader* loader, int32_t* idx_dev, void* 
 
 /* Stops the background thread and frees the loader (NULL is accepted). */
 kd_status kd_cache_loader_close(kd_cache_loader* loader);
+
+/* Streaming writer: the storing end of the teacher pass ([wiki] "사전 계산
+ * (Pre-computation) 파이프라인", steps 2-3: the teacher runs over the whole dataset
+ * and the top-K pairs of every position are stored).  Batches of rows that are on
+ * the device (such as kd_topk_cache_build's outputs) are handed over as they are
+ * produced; a background thread assembles them into shards of shard->n_tokens rows
+ * and writes each one as with kd_cache_write, named <prefix>_00000.kdc,
+ * <prefix>_00001.kdc, ... (the last shard holds the remaining rows).
+ *   shard    vocab, k, idx_bits (0: 16 when V <= 65536, else 32), val_dtype, and
+ *            n_tokens = rows per shard (>= 1);
+ *   max_batch_tokens  the most rows one kd_cache_writer_put may hand over;
+ *   depth    pinned host batch buffers in flight (2..64).
+ * Host memory: depth pinned buffers of max_batch_tokens rows plus one shard of
+ * rows; the writer allocates no device memory.  Not thread-safe: one producer per
+ * writer. */
+typedef struct kd_cache_writer kd_cache_writer;
+
+kd_status kd_cache_writer_open(const char* prefix, const kd_cache_info* shard, int64_t max_batch_tokens,
+                               int32_t depth, kd_cache_writer** out);
+
+/* Hands over `rows` rows (0 <= rows <= max_batch_tokens): idx_dev [rows, k] int32
+ * and val_dev [rows, k] val_dtype, device buffers that must stay unchanged until
+ * the copies enqueued on `stream` (hipStream_t; NULL = default) have run.  The
+ * call waits only for a free host buffer, never for the copies or the disk.
+ * Indices are checked when their shard is written; an error of the background
+ * thread (KD_ERR_IO, KD_ERR_IDX_OUT_OF_RANGE, ...) is returned by the next put and
+ * by close. */
+kd_status kd_cache_writer_put(kd_cache_writer* writer, const int32_t* idx_dev, const void* val_dev, int64_t rows,
+                              void* stream);
+
+/* Writes the last shard, stops the thread, frees the writer (NULL is accepted)
+ * and returns the first error of any shard write; *n_shards (may be NULL) gets
+ * the number of shards written. */
+kd_status kd_cache_writer_close(kd_cache_writer* writer, int64_t* n_shards);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,9 @@ Entry points (same names as the C ABI):
   on-disk cache shards (C ABI in ``include/kdcache.h``);
   :func:`kd_cache_loader_open` / :func:`kd_cache_loader_next` /
   :func:`kd_cache_loader_close` and the iterator :class:`CacheLoader` -- streaming
-  of shards to the device with prefetch.
+  of shards to the device with prefetch; :func:`kd_cache_writer_open` /
+  :func:`kd_cache_writer_put` / :func:`kd_cache_writer_close` and
+  :class:`CacheWriter` -- device batches written to shards in the background.
 """
 from __future__ import annotations
 
@@ -50,7 +52,8 @@ STATUS_NAMES = {
 EXPORTED = ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd",
             "kd_chunked_kl_fwd_ex", "kd_chunked_kl_bwd_ex", "kd_status_string", "kd_version", "kd_profile_begin", "kd_profile_end",
             "kd_cache_write", "kd_cache_info_read", "kd_cache_read", "kd_cache_loader_open",
-            "kd_cache_loader_info", "kd_cache_loader_next", "kd_cache_loader_close")
+            "kd_cache_loader_info", "kd_cache_loader_next", "kd_cache_loader_close",
+            "kd_cache_writer_open", "kd_cache_writer_put", "kd_cache_writer_close")
 
 
 class KDProblem(ctypes.Structure):
@@ -146,8 +149,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kd_cache_loader_info.argtypes = [vp, CI]
     lib.kd_cache_loader_next.argtypes = [vp, vp, vp, ctypes.POINTER(i64), vp]
     lib.kd_cache_loader_close.argtypes = [vp]
+    lib.kd_cache_writer_open.argtypes = [cp, CI, i64, i32, ctypes.POINTER(vp)]
+    lib.kd_cache_writer_put.argtypes = [vp, vp, vp, i64, vp]
+    lib.kd_cache_writer_close.argtypes = [vp, ctypes.POINTER(i64)]
     for f in ("kd_cache_write", "kd_cache_info_read", "kd_cache_read", "kd_cache_loader_open",
-              "kd_cache_loader_info", "kd_cache_loader_next", "kd_cache_loader_close"):
+              "kd_cache_loader_info", "kd_cache_loader_next", "kd_cache_loader_close",
+              "kd_cache_writer_open", "kd_cache_writer_put", "kd_cache_writer_close"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -501,6 +508,71 @@ class CacheLoader:
         if self.handle is not None:
             kd_cache_loader_close(self.handle)
             self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def kd_cache_writer_open(prefix: str, shard_tokens: int, vocab: int, k: int, val_dtype: torch.dtype,
+                         max_batch_tokens: int, depth: int = 3, idx_bits: int = 0) -> ctypes.c_void_p:
+    """Open a streaming writer of shards ``<prefix>_00000.kdc`` ... of
+    ``shard_tokens`` rows each."""
+    info = KDCacheInfo(int(shard_tokens), int(vocab), int(k), int(idx_bits), _dt(val_dtype))
+    h = ctypes.c_void_p()
+    _check(load_library().kd_cache_writer_open(os.fsencode(prefix), ctypes.byref(info), int(max_batch_tokens),
+                                               int(depth), ctypes.byref(h)), "kd_cache_writer_open")
+    return h
+
+
+def kd_cache_writer_put(handle: ctypes.c_void_p, idx_dev: torch.Tensor, val_dev: torch.Tensor) -> None:
+    """Hand over device rows ``idx_dev`` int32 [rows, K] and ``val_dev`` [rows, K];
+    the copies run on the current stream of their device.  The tensors must stay
+    unchanged until those copies have run (the next put or close waits for them
+    only as far as buffer space requires)."""
+    dev = _need_gpu(idx_dev, val_dev)
+    if idx_dev.dtype != torch.int32 or idx_dev.dim() != 2 or val_dev.shape != idx_dev.shape:
+        raise ValueError("idx must be int32 [rows, K] and val [rows, K]")
+    with torch.cuda.device(dev):
+        _check(load_library().kd_cache_writer_put(handle, _ptr(idx_dev), _ptr(val_dev), int(idx_dev.shape[0]),
+                                                  _stream(dev)), "kd_cache_writer_put")
+
+
+def kd_cache_writer_close(handle: ctypes.c_void_p) -> int:
+    """Write the last shard and free the writer; returns the number of shards."""
+    n = ctypes.c_int64(0)
+    _check(load_library().kd_cache_writer_close(handle, ctypes.byref(n)), "kd_cache_writer_close")
+    return int(n.value)
+
+
+class CacheWriter:
+    """``with CacheWriter(prefix, shard_tokens, vocab, k, torch.bfloat16, max_batch) as w:
+    w.put(idx, val)`` for each device batch; ``w.paths`` lists the shards written."""
+
+    def __init__(self, prefix: str, shard_tokens: int, vocab: int, k: int, val_dtype: torch.dtype,
+                 max_batch_tokens: int, depth: int = 3, idx_bits: int = 0):
+        self.prefix = prefix
+        self.handle = kd_cache_writer_open(prefix, shard_tokens, vocab, k, val_dtype, max_batch_tokens, depth,
+                                           idx_bits)
+        self.paths = []
+
+    def put(self, idx_dev: torch.Tensor, val_dev: torch.Tensor) -> None:
+        kd_cache_writer_put(self.handle, idx_dev, val_dev)
+
+    def close(self) -> list:
+        if self.handle is not None:
+            h, self.handle = self.handle, None
+            n = kd_cache_writer_close(h)
+            self.paths = [f"{self.prefix}_{i:05d}.kdc" for i in range(n)]
+        return self.paths
 
     def __enter__(self):
         return self

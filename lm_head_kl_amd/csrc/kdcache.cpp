@@ -449,3 +449,185 @@ extern "C" kd_status kd_cache_loader_close(kd_cache_loader* L) {
   delete L;
   return KD_OK;
 }
+
+// ---- streaming writer
+
+struct kd_cache_writer {
+  std::string prefix;
+  kd_cache_info info{};          // n_tokens = rows per full shard
+  int64_t max_batch = 0;
+  int nslots = 0;
+  struct Slot {
+    int32_t* idx = nullptr;
+    void* val = nullptr;
+    int64_t rows = 0;
+    hipEvent_t done = nullptr;
+  };
+  std::vector<Slot> slots;
+  std::vector<int32_t> sidx;     // the shard being assembled
+  std::vector<unsigned char> sval;
+  int64_t srows = 0;
+  int64_t shards_written = 0;
+  std::thread worker;
+  std::mutex mu;
+  std::condition_variable cv;
+  int64_t queued = 0, drained = 0;   // batches put / batches moved into shards
+  bool closing = false;
+  kd_status err = KD_OK;
+
+  std::string shard_path(int64_t i) const {
+    char num[32];
+    std::snprintf(num, sizeof num, "_%05lld.kdc", (long long)i);
+    return prefix + num;
+  }
+
+  kd_status flush() {
+    if (srows == 0) return KD_OK;
+    kd_cache_info in = info;
+    in.n_tokens = srows;
+    const kd_status st = kd_cache_write(shard_path(shards_written).c_str(), &in, sidx.data(), sval.data());
+    if (st == KD_OK) ++shards_written;
+    srows = 0;
+    return st;
+  }
+
+  // rows of one slot into the shard buffer, writing every shard that fills up
+  kd_status take(const Slot& s) {
+    const int64_t k = info.k, vb = val_bytes(info.val_dtype);
+    int64_t done = 0;
+    while (done < s.rows) {
+      const int64_t m = std::min(s.rows - done, info.n_tokens - srows);
+      std::memcpy(sidx.data() + srows * k, s.idx + done * k, (size_t)(m * k * 4));
+      std::memcpy(sval.data() + srows * k * vb, (const char*)s.val + done * k * vb, (size_t)(m * k * vb));
+      srows += m;
+      done += m;
+      if (srows == info.n_tokens) {
+        const kd_status st = flush();
+        if (st != KD_OK) return st;
+      }
+    }
+    return KD_OK;
+  }
+
+  void run() {
+    for (;;) {
+      int64_t b;
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        cv.wait(lk, [&] { return queued > drained || closing; });
+        if (queued == drained) break;   // closing, nothing left
+        b = drained;
+      }
+      Slot& s = slots[(size_t)(b % nslots)];
+      kd_status st = hipEventSynchronize(s.done) == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+      if (st == KD_OK) st = take(s);
+      std::lock_guard<std::mutex> lk(mu);
+      if (st != KD_OK && err == KD_OK) err = st;
+      ++drained;
+      cv.notify_all();
+    }
+    const kd_status st = flush();
+    std::lock_guard<std::mutex> lk(mu);
+    if (st != KD_OK && err == KD_OK) err = st;
+  }
+
+  void release() {
+    for (auto& s : slots) {
+      if (s.done) (void)hipEventDestroy(s.done);
+      if (s.idx) (void)hipHostFree(s.idx);
+      if (s.val) (void)hipHostFree(s.val);
+    }
+    slots.clear();
+  }
+};
+
+extern "C" kd_status kd_cache_writer_open(const char* prefix, const kd_cache_info* shard, int64_t max_batch_tokens,
+                                          int32_t depth, kd_cache_writer** out) {
+  if (!prefix || !shard || !out) return KD_ERR_NULL_POINTER;
+  *out = nullptr;
+  kd_cache_info in = *shard;
+  if (in.idx_bits == 0) in.idx_bits = in.vocab <= 65536 ? 16 : 32;
+  if (in.n_tokens < 1 || max_batch_tokens < 1 || depth < 2 || depth > 64) return KD_ERR_BAD_SHAPE;
+  const kd_status sh = check_shape(in.n_tokens, in.vocab, in.k, in.idx_bits, in.val_dtype);
+  if (sh != KD_OK) return sh;
+  if (max_batch_tokens > (int64_t(1) << 40) / in.k) return KD_ERR_BAD_SHAPE;
+  kd_cache_writer* W = new (std::nothrow) kd_cache_writer;
+  if (!W) return KD_ERR_IO;
+  W->prefix = prefix;
+  W->info = in;
+  W->max_batch = max_batch_tokens;
+  W->nslots = depth;
+  kd_status st = KD_OK;
+  try {
+    W->sidx.resize((size_t)(in.n_tokens * in.k));
+    W->sval.resize((size_t)(in.n_tokens * in.k * val_bytes(in.val_dtype)));
+  } catch (const std::bad_alloc&) {
+    st = KD_ERR_IO;
+  }
+  W->slots.resize((size_t)depth);
+  const size_t ib = (size_t)(max_batch_tokens * in.k * 4);
+  const size_t vb = (size_t)(max_batch_tokens * in.k * val_bytes(in.val_dtype));
+  for (auto& s : W->slots) {
+    if (st != KD_OK) break;
+    if (hipHostMalloc((void**)&s.idx, ib, hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc(&s.val, vb, hipHostMallocDefault) != hipSuccess ||
+        hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess)
+      st = KD_ERR_NO_DEVICE;
+  }
+  if (st == KD_OK) {
+    try {
+      W->worker = std::thread([W] { W->run(); });
+    } catch (...) {
+      st = KD_ERR_IO;
+    }
+  }
+  if (st != KD_OK) {
+    W->release();
+    delete W;
+    return st;
+  }
+  *out = W;
+  return KD_OK;
+}
+
+extern "C" kd_status kd_cache_writer_put(kd_cache_writer* W, const int32_t* idx_dev, const void* val_dev,
+                                         int64_t rows, void* stream) {
+  if (!W) return KD_ERR_NULL_POINTER;
+  if (rows < 0 || rows > W->max_batch) return KD_ERR_BAD_SHAPE;
+  if (rows == 0) return KD_OK;
+  if (!idx_dev || !val_dev) return KD_ERR_NULL_POINTER;
+  std::unique_lock<std::mutex> lk(W->mu);
+  if (W->err != KD_OK) return W->err;
+  // a slot is free once the worker has moved its previous batch into a shard
+  W->cv.wait(lk, [&] { return W->queued - W->drained < W->nslots || W->err != KD_OK; });
+  if (W->err != KD_OK) return W->err;
+  auto& s = W->slots[(size_t)(W->queued % W->nslots)];
+  lk.unlock();
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t k = W->info.k;
+  if (hipMemcpyAsync(s.idx, idx_dev, (size_t)(rows * k * 4), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(s.val, val_dev, (size_t)(rows * k * val_bytes(W->info.val_dtype)), hipMemcpyDeviceToHost,
+                     st) != hipSuccess ||
+      hipEventRecord(s.done, st) != hipSuccess)
+    return KD_ERR_LAUNCH;
+  s.rows = rows;
+  lk.lock();
+  ++W->queued;
+  W->cv.notify_all();
+  return KD_OK;
+}
+
+extern "C" kd_status kd_cache_writer_close(kd_cache_writer* W, int64_t* n_shards) {
+  if (!W) return KD_OK;
+  {
+    std::lock_guard<std::mutex> lk(W->mu);
+    W->closing = true;
+    W->cv.notify_all();
+  }
+  if (W->worker.joinable()) W->worker.join();
+  const kd_status st = W->err;
+  if (n_shards) *n_shards = W->shards_written;
+  W->release();
+  delete W;
+  return st;
+}

@@ -201,3 +201,23 @@ def test_loader_argument_checks(lib, tmp_path):
     if not torch.cuda.is_available():
         st, h = open_status([a])
         assert st == KD_ERR_NO_DEVICE and not h.value
+
+
+def test_writer_argument_errors_before_any_device_call():
+    """The streaming writer validates its arguments before touching the HIP runtime
+    (these run on a host without a GPU)."""
+    import ctypes
+    lib = kd.load_library()
+    out = ctypes.c_void_p()
+    info = kd.KDCacheInfo(1000, 32000, 16, 0, kd.KD_BF16)
+    assert lib.kd_cache_writer_open(None, ctypes.byref(info), 100, 2, ctypes.byref(out)) == 1
+    assert lib.kd_cache_writer_open(b"/tmp/x", None, 100, 2, ctypes.byref(out)) == 1
+    for bad, st in ((kd.KDCacheInfo(0, 32000, 16, 0, kd.KD_BF16), 2),        # no rows per shard
+                    (kd.KDCacheInfo(1000, 100000, 16, 16, kd.KD_BF16), 2),   # 16-bit indices, V > 65536
+                    (kd.KDCacheInfo(1000, 32000, 0, 0, kd.KD_BF16), 2),      # K = 0
+                    (kd.KDCacheInfo(1000, 32000, 16, 0, 7), 3)):             # unknown value dtype
+        assert lib.kd_cache_writer_open(b"/tmp/x", ctypes.byref(bad), 100, 2, ctypes.byref(out)) == st
+    assert lib.kd_cache_writer_open(b"/tmp/x", ctypes.byref(info), 0, 2, ctypes.byref(out)) == 2
+    assert lib.kd_cache_writer_open(b"/tmp/x", ctypes.byref(info), 100, 1, ctypes.byref(out)) == 2
+    assert lib.kd_cache_writer_put(None, None, None, 1, None) == 1
+    assert lib.kd_cache_writer_close(None, None) == 0

@@ -93,3 +93,63 @@ def test_loss_from_loaded_cache_is_identical(tmp_path):
     torch.cuda.synchronize()
     assert torch.equal(li, idx) and torch.equal(_bits(lv), _bits(val))
     assert torch.equal(loss_a, loss_b) and torch.equal(lse_a, lse_b)
+
+
+def test_writer_pipeline_build_then_store(tmp_path):
+    """The offline pass at small scale: the teacher cache is built on the GPU batch
+    by batch, each batch handed to the streaming writer without a host sync, and
+    the shards (1,500 rows each; the last one shorter) read back bit-exactly,
+    through kd_cache_read and through the loader."""
+    print("[case] writer pipeline", flush=True)
+    n, d, v, k, batch, shard = 5000, 64, 3000, 24, 700, 1500
+    p = kd_synth.small_problem(n, d, v, seed=51)
+    to_dev = lambda x: torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(DEV)
+    h, wt = to_dev(p["H"]), to_dev(p["WT"])
+    prefix = str(tmp_path / "cache")
+    built_i, built_v = [], []
+    with kd.CacheWriter(prefix, shard, v, k, torch.bfloat16, batch) as wr:
+        for r0 in range(0, n, batch):
+            i, val = kd.kd_topk_cache_build(h[r0:r0 + batch].contiguous(), wt, k)
+            wr.put(i, val)
+            built_i.append(i)
+            built_v.append(val)
+    assert wr.paths == [f"{prefix}_{j:05d}.kdc" for j in range(4)]
+    sizes = [kd.kd_cache_info_read(path)["n_tokens"] for path in wr.paths]
+    assert sizes == [1500, 1500, 1500, 500]
+    assert all(kd.kd_cache_info_read(path)["idx_bits"] == 16 for path in wr.paths)
+    want_i = torch.cat(built_i).cpu()
+    want_v = torch.cat(built_v).cpu()
+    got = [kd.kd_cache_read(path) for path in wr.paths]
+    assert torch.equal(torch.cat([g[0] for g in got]), want_i)
+    assert torch.equal(_bits(torch.cat([g[1] for g in got])), _bits(want_v))
+    with kd.CacheLoader(wr.paths, 1024, 2, DEV) as ld:
+        li = torch.cat([b[0] for b in ld]).cpu()
+    assert torch.equal(li, want_i)
+
+
+def test_writer_f32_and_index_errors(tmp_path):
+    """float32 values with 32-bit indices round-trip; an out-of-range index fails
+    its shard, and the error comes back from the next put and from close."""
+    idx, val = _cache(300, 8, 100000, torch.float32, 7)
+    prefix = str(tmp_path / "f")
+    with kd.CacheWriter(prefix, 128, 100000, 8, torch.float32, 100, depth=2) as wr:
+        for r0 in range(0, 300, 100):
+            wr.put(idx[r0:r0 + 100].to(DEV), val[r0:r0 + 100].to(DEV))
+    got = [kd.kd_cache_read(path) for path in wr.paths]
+    assert [kd.kd_cache_info_read(path)["idx_bits"] for path in wr.paths] == [32, 32, 32]
+    assert torch.equal(torch.cat([g[0] for g in got]), idx)
+    assert torch.equal(_bits(torch.cat([g[1] for g in got])), _bits(val))
+
+    bad = idx.clone()
+    bad[5, 3] = 100000
+    wr2 = kd.CacheWriter(str(tmp_path / "bad"), 10, 100000, 8, torch.float32, 100, depth=2)
+    wr2.put(bad[:100].to(DEV), val[:100].to(DEV))
+    # with two buffers the third put waits for the first batch's shards, whose
+    # write has failed by then
+    with pytest.raises(kd.KDError) as e:
+        for _ in range(2):
+            wr2.put(idx[:100].to(DEV), val[:100].to(DEV))
+    assert e.value.status == 10
+    with pytest.raises(kd.KDError) as e:
+        wr2.close()
+    assert e.value.status == 10

@@ -4,6 +4,8 @@
  * top-K cache, runs the forward and the backward, and writes the results.  It
  * then writes the cache to two shard files in DIR (include/kdcache.h), streams them
  * back to the device with the loader and runs the forward again on that copy.
+ * It also streams the device cache to shards with the streaming writer (two puts,
+ * shards of N/2 + 1 rows) and compares what kd_cache_read returns with it.
  * Last, the loss options (kd_loss_opts): labels[i] = -100 (ignored) when
  * i % 7 == 3, else (131 i) mod V, with a cross-entropy weight of 0.25, through the
  * _ex forward and backward:
@@ -13,7 +15,8 @@
  *        bits (uint16), teacher hidden states = H
  *   OUT: int32 status; then idx [N*K] int32, val [N*K] bf16 bits, loss float,
  *        lse [N] float, dH [N*d] float, dW [V*d] float, loss from the reloaded cache float,
- *        then with the options: loss float, dH [N*d] float, dW [V*d] float
+ *        then with the options: loss float, dH [N*d] float, dW [V*d] float,
+ *        then int32 writer_ok (1 when the writer's shards hold the cache exactly)
  *
  * Exit status 0 on success; on a library error the kd_status is printed with
  * kd_status_string() and the exit status is 1.
@@ -169,13 +172,43 @@ int main(int argc, char** argv) {
   HIP_OK(hipMemcpy(dhh3, ddh, 4 * nh, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(dwh3, ddw, 4 * nw, hipMemcpyDeviceToHost));
 
+  /* the streaming writer: the device cache in two puts, shards of N/2 + 1 rows */
+  int32_t writer_ok = 0;
+  {
+    char wprefix[4096];
+    snprintf(wprefix, sizeof wprefix, "%s/w", argv[3]);
+    kd_cache_info shard = {N / 2 + 1, V, K, 0, KD_BF16};
+    kd_cache_writer* wr = NULL;
+    KD_OK_OR_FAIL(kd_cache_writer_open(wprefix, &shard, N - N / 2, 2, &wr));
+    KD_OK_OR_FAIL(kd_cache_writer_put(wr, (const int32_t*)didx, dval, N / 2, st));
+    KD_OK_OR_FAIL(kd_cache_writer_put(wr, (const int32_t*)didx + (N / 2) * K, (const uint16_t*)dval + (N / 2) * K,
+                                      N - N / 2, st));
+    int64_t n_shards = 0;
+    KD_OK_OR_FAIL(kd_cache_writer_close(wr, &n_shards));
+    int32_t* ridx = malloc(4 * nk + 4);
+    uint16_t* rval = malloc(2 * nk + 2);
+    if (!ridx || !rval) return 2;
+    int64_t row = 0;
+    for (int64_t i = 0; i < n_shards; ++i) {
+      char path[4200];
+      snprintf(path, sizeof path, "%s_%05lld.kdc", wprefix, (long long)i);
+      kd_cache_info si;
+      KD_OK_OR_FAIL(kd_cache_info_read(path, &si));
+      KD_OK_OR_FAIL(kd_cache_read(path, 0, si.n_tokens, ridx + row * K, rval + row * K));
+      row += si.n_tokens;
+    }
+    writer_ok = n_shards == 2 && row == N && memcmp(ridx, idx, 4 * nk) == 0 && memcmp(rval, val, 2 * nk) == 0;
+    free(ridx);
+    free(rval);
+  }
+
   FILE* fo = fopen(argv[2], "wb");
   if (!fo) return 2;
   const int32_t ok = 0;
   if (!write_all(fo, &ok, 4) || !write_all(fo, idx, 4 * nk) || !write_all(fo, val, 2 * nk) ||
       !write_all(fo, &loss, 4) || !write_all(fo, lse, 4 * (size_t)N) || !write_all(fo, dhh, 4 * nh) ||
       !write_all(fo, dwh, 4 * nw) || !write_all(fo, &loss2, 4) || !write_all(fo, &loss3, 4) ||
-      !write_all(fo, dhh3, 4 * nh) || !write_all(fo, dwh3, 4 * nw))
+      !write_all(fo, dhh3, 4 * nh) || !write_all(fo, dwh3, 4 * nw) || !write_all(fo, &writer_ok, 4))
     return 2;
   fclose(fo);
   printf("kd_client: N=%lld d=%lld V=%lld K=%d loss=%.6f (kd_version %d)\n", (long long)N, (long long)d,

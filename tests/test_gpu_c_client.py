@@ -4,7 +4,8 @@ teacher cache, runs the forward and the backward; its outputs must match the
 float64 oracle on the same inputs.  It also writes the cache to shard files and
 streams them back with the loader (include/kdcache.h): the loss from that copy must
 be the same float.  Last it runs the _ex calls with a padding mask and a hard-label
-mix (kd_loss_opts), checked against ``oracle.variant_forward`` / ``variant_backward``."""
+mix (kd_loss_opts), checked against ``oracle.variant_forward`` / ``variant_backward``,
+and streams the device cache to shards with the streaming writer."""
 import os
 import subprocess
 
@@ -54,7 +55,9 @@ def test_c_client_matches_oracle(tmp_path):
     g_loss3 = float(take(np.float32, 1)[0])
     g_dh3 = take(np.float32, n * d).reshape(n, d)
     g_dw3 = take(np.float32, v * d).reshape(v, d)
+    writer_ok = take(np.int32, 1)[0]
     assert off == len(buf)
+    assert writer_ok == 1                                 # the streaming writer's shards hold the cache
     assert np.float32(g_loss) == g_loss2                 # same cache bytes, same loss
     assert (tmp_path / "c0.kdc").exists() and (tmp_path / "c1.kdc").exists()
 

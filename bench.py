@@ -159,7 +159,7 @@ def sweep(kd, torch, np, kd_synth, steps, warmup):
     return 0
 
 
-def cache_io(kd, torch, idx, val, vocab, shards=4, batch=16384, prefetch=3):
+def cache_io(kd, torch, idx, val, vocab, shards=4, batch=16384, prefetch=3, with_paths=None):
     """Write the built cache to shards in a temporary directory and stream it back
     to the device with the loader (the files were just written, so this measures the
     page cache and the upload path, not a disk).  Checks the streamed cache is the
@@ -199,12 +199,48 @@ def cache_io(kd, torch, idx, val, vocab, shards=4, batch=16384, prefetch=3):
                                                                          else torch.int32)))
         if not exact or row != n:
             raise RuntimeError("cache streamed back through the loader differs from the cache written")
-        return {"bytes": nbytes, "shards": shards, "idx_bits": bits, "batch_tokens": batch,
-                "write_gbs": nbytes / t_write / 1e9, "load_gbs": nbytes / t_load / 1e9,
-                "load_tokens_per_s": n / t_load, "exact": exact,
-                "note": "files in the page cache; host->device through pinned buffers"}
+        out = {"bytes": nbytes, "shards": shards, "idx_bits": bits, "batch_tokens": batch,
+               "write_gbs": nbytes / t_write / 1e9, "load_gbs": nbytes / t_load / 1e9,
+               "load_tokens_per_s": n / t_load, "exact": exact,
+               "note": "files in the page cache; host->device through pinned buffers"}
+        if with_paths is not None:
+            out["loss_fed_by_loader"] = with_paths(paths)
+        return out
     finally:
         shutil.rmtree(d, ignore_errors=True)
+
+
+def loader_fed_steps(kd, torch, h, wd, idx, val, w, dh_dtype, paths, batch=16384):
+    """Training fed from the cache files: the loader streams the shards in batches of
+    `batch` tokens while each batch's forward and backward run on the GPU.  The same
+    per-batch loop with the cache already in device memory is timed beside it, so
+    the difference is what reading the cache costs the loss."""
+    def step(i, v, r0, rows):
+        hb = h[r0:r0 + rows]
+        loss, lse, _ = kd.kd_chunked_kl_fwd(hb, wd, i, v, w.tau)
+        kd.kd_chunked_kl_bwd(hb, wd, i, v, w.tau, lse, None, dh_dtype=dh_dtype)
+
+    n = h.shape[0]
+    step(idx[:batch], val[:batch], 0, min(batch, n))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r0 in range(0, n, batch):
+        rows = min(batch, n - r0)
+        step(idx[r0:r0 + rows], val[r0:r0 + rows], r0, rows)
+    torch.cuda.synchronize()
+    t_mem = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    r0 = 0
+    with kd.CacheLoader(paths, batch, 3, str(h.device)) as ld:
+        for i, v in ld:
+            step(i, v, r0, i.shape[0])
+            r0 += i.shape[0]
+    torch.cuda.synchronize()
+    t_ld = time.perf_counter() - t0
+    if r0 != n:
+        raise RuntimeError("the loader handed out a different number of rows than the cache holds")
+    return {"tokens_per_s": n / t_ld, "from_memory_tokens_per_s": n / t_mem, "batch_tokens": batch,
+            "ratio": round(t_mem / t_ld, 4)}
 
 
 def cache_pipeline(kd, torch, h, wt, k, vocab, ref_idx, ref_val, batch=32768, shard=32768):
@@ -426,9 +462,13 @@ def main() -> int:
 
     cio = None
     if not args.no_cache_io:
-        cio = cache_io(kd, torch, idx, val, w.vocab)
+        cio = cache_io(kd, torch, idx, val, w.vocab,
+                       with_paths=lambda paths: loader_fed_steps(kd, torch, h, wd, idx, val, w, dh_dtype, paths))
         log(f"cache io: {cio['bytes'] / 1e6:.1f} MB in {cio['shards']} shards; write {cio['write_gbs']:.2f} GB/s, "
             f"loader to device {cio['load_gbs']:.2f} GB/s = {cio['load_tokens_per_s']:.0f} tokens/s")
+        lf = cio["loss_fed_by_loader"]
+        log(f"loss fed by the loader ({lf['batch_tokens']}-token batches): {lf['tokens_per_s']:.0f} tokens/s, "
+            f"from device memory {lf['from_memory_tokens_per_s']:.0f} tokens/s (ratio {lf['ratio']:.3f})")
         wt = to_dev(kd_synth.teacher_head(w))
         cio["pipeline"] = cache_pipeline(kd, torch, h, wt, k, w.vocab, idx, val)
         del wt

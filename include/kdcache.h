@@ -136,7 +136,9 @@ kd_status kd_cache_writer_put(kd_cache_writer* writer, const int32_t* idx_dev, c
 
 /* Writes the last shard, stops the thread, frees the writer (NULL is accepted)
  * and returns the first error of any shard write; *n_shards (may be NULL) gets
- * the number of shards written. */
+ * the number of shards written.  After an error no further shard is written, so
+ * the n_shards files on disk always hold the first n_shards * shard->n_tokens
+ * rows handed over, complete and in order. */
 kd_status kd_cache_writer_close(kd_cache_writer* writer, int64_t* n_shards);
 
 #ifdef __cplusplus

@@ -568,10 +568,14 @@ class CacheWriter:
         kd_cache_writer_put(self.handle, idx_dev, val_dev)
 
     def close(self) -> list:
+        """Write the last shard and free the writer.  ``paths`` is set before an
+        error is raised: the shards written before it are complete and in order."""
         if self.handle is not None:
             h, self.handle = self.handle, None
-            n = kd_cache_writer_close(h)
-            self.paths = [f"{self.prefix}_{i:05d}.kdc" for i in range(n)]
+            n = ctypes.c_int64(0)
+            st = load_library().kd_cache_writer_close(h, ctypes.byref(n))
+            self.paths = [f"{self.prefix}_{i:05d}.kdc" for i in range(n.value)]
+            _check(st, "kd_cache_writer_close")
         return self.paths
 
     def __enter__(self):

@@ -509,7 +509,11 @@ struct kd_cache_writer {
     return KD_OK;
   }
 
+  // After the first error no further shard is written (a failed shard leaves no
+  // file), so the shards on disk are always the leading rows, complete and in order;
+  // later batches are only drained.
   void run() {
+    bool failed = false;
     for (;;) {
       int64_t b;
       {
@@ -520,13 +524,14 @@ struct kd_cache_writer {
       }
       Slot& s = slots[(size_t)(b % nslots)];
       kd_status st = hipEventSynchronize(s.done) == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
-      if (st == KD_OK) st = take(s);
+      if (st == KD_OK && !failed) st = take(s);
+      failed = failed || st != KD_OK;
       std::lock_guard<std::mutex> lk(mu);
       if (st != KD_OK && err == KD_OK) err = st;
       ++drained;
       cv.notify_all();
     }
-    const kd_status st = flush();
+    const kd_status st = failed ? KD_OK : flush();
     std::lock_guard<std::mutex> lk(mu);
     if (st != KD_OK && err == KD_OK) err = st;
   }

@@ -140,16 +140,24 @@ def test_writer_f32_and_index_errors(tmp_path):
     assert torch.equal(torch.cat([g[0] for g in got]), idx)
     assert torch.equal(_bits(torch.cat([g[1] for g in got])), _bits(val))
 
+    # the bad index is in row 25, i.e. in the third shard of 10 rows
     bad = idx.clone()
-    bad[5, 3] = 100000
-    wr2 = kd.CacheWriter(str(tmp_path / "bad"), 10, 100000, 8, torch.float32, 100, depth=2)
+    bad[25, 3] = 100000
+    bdir = tmp_path / "bad"
+    bdir.mkdir()
+    wr2 = kd.CacheWriter(str(bdir / "b"), 10, 100000, 8, torch.float32, 100, depth=2)
     wr2.put(bad[:100].to(DEV), val[:100].to(DEV))
     # with two buffers the third put waits for the first batch's shards, whose
     # write has failed by then
     with pytest.raises(kd.KDError) as e:
         for _ in range(2):
-            wr2.put(idx[:100].to(DEV), val[:100].to(DEV))
+            wr2.put(idx[100:200].to(DEV), val[100:200].to(DEV))
     assert e.value.status == 10
     with pytest.raises(kd.KDError) as e:
         wr2.close()
     assert e.value.status == 10
+    # nothing is written after the failed shard: the two before it, complete
+    assert wr2.paths == [str(bdir / "b_00000.kdc"), str(bdir / "b_00001.kdc")]
+    assert sorted(p.name for p in bdir.iterdir()) == ["b_00000.kdc", "b_00001.kdc"]
+    got = [kd.kd_cache_read(path) for path in wr2.paths]
+    assert torch.equal(torch.cat([g[0] for g in got]), idx[:20])

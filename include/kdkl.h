@@ -55,6 +55,10 @@
  *     synchronisation. The library never aborts, prints or throws.
  *   - Shape domain: N >= 0, d >= 8 with d % 8 == 0, 1 <= V <= 2097088 (2^21 - 64),
  *     1 <= K <= min(V, 65535) (the cache build: K <= 4096), tau finite and > 0.
+ *     Also N <= 2^31 - 256, d <= 2^20, chunk_tokens >= 0, and the chunk as used
+ *     (chunk_tokens or the default, rounded up to 256, and at most N rounded up to
+ *     256) at most 2096896 tokens: 256 rows of every operand, the chunk-strided
+ *     transposed ones included, then stay within 2^31 bytes.
  *   - Cached indices must lie in [0, V). An out-of-range index is skipped by the
  *     kernels (no out-of-bounds access); it makes that row's KL NaN, and when the
  *     environment variable KD_CHECK=1 is set the forward call synchronises the
@@ -217,7 +221,8 @@ typedef struct {
 kd_status kd_profile_begin(void);
 
 /* Ends the session; writes up to `max` entries to `out` and the number of kernel
- * kinds seen to *n. Returns KD_ERR_LAUNCH if an event could not be read. */
+ * kinds seen to *n. Returns KD_ERR_LAUNCH if an event could not be created, recorded
+ * or read (the launches it would have timed are left out of the entries). */
 kd_status kd_profile_end(kd_kernel_stat* out, int max, int* n);
 
 /* Library ABI version (major * 100 + minor). */

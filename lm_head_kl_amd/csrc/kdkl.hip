@@ -74,6 +74,15 @@ struct Layout {
 
 bool mul_ok(int64_t a, int64_t b, int64_t lim = INT64_MAX / 4) { return a == 0 || b <= lim / a; }
 
+// The int a C caller stored in an enum argument, read without loading it as the
+// enum type (whose C++ value range may not hold it).
+template <typename E> int enum_bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 kd_status validate(kd_op op, const kd_problem* p, Plan* pl) {
   if (!p) return KD_ERR_NULL_POINTER;
   if (p->x_dtype != KD_F32 && p->x_dtype != KD_BF16) return KD_ERR_BAD_DTYPE;
@@ -205,6 +214,7 @@ struct ProfRec {
 };
 struct Prof {
   bool on = false;
+  bool failed = false;   // an event could not be created or recorded in this session
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
   std::vector<std::string> kinds;
@@ -237,16 +247,24 @@ template <typename F>
 kd_status launch(const char* kind, double flops, double bytes, hipStream_t st, F&& f) {
   Prof& p = prof();
   hipEvent_t a = nullptr, b = nullptr;
+  bool timed = false;
   if (p.on) {
     a = prof_event();
     b = prof_event();
-    if (a && b) hipEventRecord(a, st);
+    timed = a && b && hipEventRecord(a, st) == hipSuccess;
   }
   f();
   const kd_status s = launched();
-  if (p.on && a && b) {
-    hipEventRecord(b, st);
-    p.recs.push_back(ProfRec{prof_kind(kind), a, b, flops, bytes});
+  if (p.on) {
+    timed = timed && hipEventRecord(b, st) == hipSuccess;
+    if (timed) {
+      p.recs.push_back(ProfRec{prof_kind(kind), a, b, flops, bytes});
+    } else {
+      // the launch stays untimed; its events go back to the pool and the session reports the failure
+      p.failed = true;
+      if (a) p.pool.push_back(a);
+      if (b) p.pool.push_back(b);
+    }
   }
   return s;
 }
@@ -555,9 +573,12 @@ kd_status topk_impl(const Plan& pl, const Layout& L, const void* ht, const void*
 
 extern "C" {
 
-kd_status kd_workspace_size(kd_op op, const kd_problem* p, size_t* bytes) {
+kd_status kd_workspace_size(kd_op op_in, const kd_problem* p, size_t* bytes) {
   if (!bytes) return KD_ERR_NULL_POINTER;
-  if (op != KD_OP_TOPK_BUILD && op != KD_OP_KL_FWD && op != KD_OP_KL_BWD) return KD_ERR_BAD_SHAPE;
+  // a C caller may pass any int; it is read as one before it is used as a kd_op
+  const int raw = enum_bits(op_in);
+  if (raw != KD_OP_TOPK_BUILD && raw != KD_OP_KL_FWD && raw != KD_OP_KL_BWD) return KD_ERR_BAD_SHAPE;
+  const kd_op op = (kd_op)raw;
   Plan pl;
   KD_TRY(validate(op, p, &pl));
   Layout L;
@@ -671,8 +692,8 @@ kd_status kd_chunked_kl_bwd_ex(const kd_problem* p, const kd_loss_opts* opts, co
   return bwd_entry(p, opts, h, w, idx, val, lse, grad_loss, dh_out, dw_out, ws, ws_bytes, stream);
 }
 
-const char* kd_status_string(kd_status s) {
-  switch (s) {
+const char* kd_status_string(kd_status s_in) {
+  switch (enum_bits(s_in)) {
     case KD_OK: return "ok";
     case KD_ERR_NULL_POINTER: return "a required pointer is NULL";
     case KD_ERR_BAD_SHAPE: return "a size is outside the supported domain";
@@ -702,6 +723,7 @@ kd_status kd_profile_begin(void) {
   }
   p.recs.clear();
   p.kinds.clear();
+  p.failed = false;
   p.on = true;
   return KD_OK;
 }
@@ -709,7 +731,7 @@ kd_status kd_profile_begin(void) {
 kd_status kd_profile_end(kd_kernel_stat* out, int max, int* n) {
   Prof& p = prof();
   p.on = false;
-  kd_status st = KD_OK;
+  kd_status st = p.failed ? KD_ERR_LAUNCH : KD_OK;
   std::vector<kd_kernel_stat> agg(p.kinds.size());
   for (size_t i = 0; i < p.kinds.size(); ++i) {
     std::memset(&agg[i], 0, sizeof(kd_kernel_stat));

@@ -79,14 +79,23 @@ def test_workspace_size_rejects_bad_problems(lib, kw, status):
 
 @pytest.mark.parametrize("x_dtype", [kd.KD_BF16, kd.KD_F32])
 def test_domain_limits_are_exact(lib, x_dtype):
-    """The header's largest V (2,097,088) and K (65,535; 4,096 for the cache build)
-    are accepted by every call and one more is refused."""
+    """The header's largest V (2,097,088), K (65,535; 4,096 for the cache build),
+    d, N and chunk are accepted by every call and one more is refused."""
     for op in (kd.KD_OP_TOPK_BUILD, kd.KD_OP_KL_FWD, kd.KD_OP_KL_BWD):
         assert _ws(lib, op, _P(v=2097088, x_dtype=x_dtype))[0] == 0, op
         assert _ws(lib, op, _P(v=2097089, x_dtype=x_dtype))[0] == 2, op
         kmax = 4096 if op == kd.KD_OP_TOPK_BUILD else 65535
         assert _ws(lib, op, _P(v=70000, k=kmax, x_dtype=x_dtype))[0] == 0, op
         assert _ws(lib, op, _P(v=70000, k=kmax + 1, x_dtype=x_dtype))[0] == 2, op
+        # d <= 2^20, N <= 2^31 - 256, and the chunk as used <= 2,096,896 tokens
+        assert _ws(lib, op, _P(d=1 << 20, x_dtype=x_dtype))[0] == 0, op
+        assert _ws(lib, op, _P(d=(1 << 20) + 8, x_dtype=x_dtype))[0] == 2, op
+        assert _ws(lib, op, _P(n=(1 << 31) - 256, x_dtype=x_dtype))[0] == 0, op
+        assert _ws(lib, op, _P(n=(1 << 31) - 255, x_dtype=x_dtype))[0] == 2, op
+        assert _ws(lib, op, _P(n=1 << 22, chunk_tokens=2096896, x_dtype=x_dtype))[0] == 0, op
+        assert _ws(lib, op, _P(n=1 << 22, chunk_tokens=2096897, x_dtype=x_dtype))[0] == 2, op
+        assert _ws(lib, op, _P(n=2096896, chunk_tokens=(1 << 31) - 1, x_dtype=x_dtype))[0] == 0, op
+        assert _ws(lib, op, _P(n=2096897, chunk_tokens=(1 << 31) - 1, x_dtype=x_dtype))[0] == 2, op
 
 
 def test_workspace_size_null_and_bad_op(lib):

@@ -215,6 +215,21 @@ def _need_gpu(*ts: torch.Tensor) -> torch.device:
     return dev
 
 
+def _loss_inputs(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor,
+                 lse: Optional[torch.Tensor] = None) -> Tuple[int, int, int, int]:
+    """Shapes and dtypes of the loss's inputs, checked before any pointer is taken:
+    the library sees only pointers and the sizes passed here.  Returns (N, d, V, K)."""
+    if h.dim() != 2 or w.dim() != 2 or w.shape[1] != h.shape[1]:
+        raise ValueError(f"h must be [N, d] and w [V, d]; got {tuple(h.shape)} and {tuple(w.shape)}")
+    if h.dtype != w.dtype or h.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"h and w must share one dtype, bfloat16 or float32; got {h.dtype} and {w.dtype}")
+    if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != h.shape[0] or val.shape != idx.shape:
+        raise ValueError("idx must be int32 [N, K] and val [N, K]")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (h.shape[0],)):
+        raise ValueError("lse must be float32 [N]")
+    return h.shape[0], h.shape[1], w.shape[0], idx.shape[1]
+
+
 def _workspace(op: int, prob: KDProblem, device: torch.device) -> torch.Tensor:
     return torch.empty(max(256, workspace_size(op, prob)), dtype=torch.uint8, device=device)
 
@@ -223,12 +238,12 @@ def kd_topk_cache_build(h_t: torch.Tensor, w_t: torch.Tensor, k: int, chunk_toke
                         ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Exact top-K teacher cache.  Returns ``(idx int32 [N,K], val [N,K])``; ``val``
     has the inputs' dtype (bf16 for bf16 heads, float32 for float32 heads)."""
+    if h_t.dim() != 2 or w_t.dim() != 2 or w_t.shape[1] != h_t.shape[1] or w_t.dtype != h_t.dtype:
+        raise ValueError("h_t must be [N, d] and w_t [V, d], of one dtype")
     dev = _need_gpu(h_t, w_t)
     n, d = h_t.shape
     v = w_t.shape[0]
     xdt = _dt(h_t.dtype)
-    if _dt(w_t.dtype) != xdt or w_t.shape[1] != d:
-        raise ValueError("h_t / w_t dtype or shape mismatch")
     prob = make_problem(n, d, v, k, 1.0, xdt, xdt, KD_F32, chunk_tokens)
     idx = torch.empty((n, k), dtype=torch.int32, device=dev)
     val = torch.empty((n, k), dtype=h_t.dtype, device=dev)
@@ -259,14 +274,9 @@ def kd_chunked_kl_fwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: 
     With ``labels`` (int32 [N]), rows labelled ``ignore_index`` are left out and
     the mean runs over the others; ``ce_weight`` a mixes in the cross-entropy
     with the labels: row term ``(1 - a) KL + a CE`` (``rows`` holds those terms)."""
+    n, d, v, k = _loss_inputs(h, w, idx, val)
     dev = _need_gpu(h, w, idx, val, labels)
-    n, d = h.shape
-    v = w.shape[0]
-    k = idx.shape[1]
-    xdt = _dt(h.dtype)
-    if idx.dtype != torch.int32 or val.shape != idx.shape or idx.shape[0] != n:
-        raise ValueError("idx must be int32 [N, K] and val [N, K]")
-    prob = make_problem(n, d, v, k, tau, xdt, _dt(val.dtype), KD_F32, chunk_tokens)
+    prob = make_problem(n, d, v, k, tau, _dt(h.dtype), _dt(val.dtype), KD_F32, chunk_tokens)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     lse = torch.empty((n,), dtype=torch.float32, device=dev)
     rows = torch.empty((n,), dtype=torch.float32, device=dev) if with_rows else None
@@ -292,10 +302,8 @@ def kd_chunked_kl_bwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: 
     """Returns ``(dH [N,d] dh_dtype, dW [V,d] float32)`` for upstream gradient
     ``grad`` (a device scalar; None means 1).  ``labels`` / ``ignore_index`` /
     ``ce_weight`` must be those of the forward call."""
+    n, d, v, k = _loss_inputs(h, w, idx, val, lse)
     dev = _need_gpu(h, w, idx, val, lse, grad, labels)
-    n, d = h.shape
-    v = w.shape[0]
-    k = idx.shape[1]
     if grad is not None and (grad.dtype != torch.float32 or grad.numel() != 1):
         raise ValueError("grad must be a float32 scalar tensor")
     prob = make_problem(n, d, v, k, tau, _dt(h.dtype), _dt(val.dtype), _dt(dh_dtype), chunk_tokens)
@@ -406,6 +414,21 @@ class ChunkedTopKKLLoss(torch.nn.Module):
 
 _VAL_TORCH = {KD_F32: torch.float32, KD_BF16: torch.bfloat16}
 
+# open loader and writer handles -> (rows one call moves at most, K, value dtype), so
+# that the device tensors of next/put are checked against them before a copy is
+# enqueued (the library sees only pointers)
+_HANDLES = {}
+
+
+def _batch_tensors(handle: ctypes.c_void_p, idx: torch.Tensor, val: torch.Tensor, where: str) -> int:
+    spec = _HANDLES.get(handle.value if handle is not None else None)
+    if spec is None:
+        raise ValueError(f"{where}: not an open handle")
+    rows, k, vdt = spec
+    if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[1] != k or val.shape != idx.shape or val.dtype != vdt:
+        raise ValueError(f"{where}: idx must be int32 [rows, {k}] and val {vdt} [rows, {k}]")
+    return rows
+
 
 def _host(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
     if t.is_cuda or t.dtype != dtype or not t.is_contiguous():
@@ -452,6 +475,8 @@ def kd_cache_loader_open(paths, batch_tokens: int, prefetch: int = 2) -> ctypes.
     h = ctypes.c_void_p()
     _check(load_library().kd_cache_loader_open(arr, len(enc), int(batch_tokens), int(prefetch), ctypes.byref(h)),
            "kd_cache_loader_open")
+    info = kd_cache_loader_info(h)
+    _HANDLES[h.value] = (min(int(batch_tokens), max(info["n_tokens"], 1)), info["k"], _VAL_TORCH[info["val_dtype"]])
     return h
 
 
@@ -464,7 +489,11 @@ def kd_cache_loader_info(handle: ctypes.c_void_p) -> dict:
 
 def kd_cache_loader_next(handle: ctypes.c_void_p, idx_dev: torch.Tensor, val_dev: torch.Tensor) -> int:
     """Enqueue the next batch's copies into the device tensors (on the current
-    stream of their device); returns its row count, 0 at the end."""
+    stream of their device); returns its row count, 0 at the end.  The tensors
+    hold at least one batch: idx int32 [>= batch_tokens, K], val [same]."""
+    rows_max = _batch_tensors(handle, idx_dev, val_dev, "kd_cache_loader_next")
+    if idx_dev.shape[0] < rows_max:
+        raise ValueError(f"kd_cache_loader_next: the tensors hold {idx_dev.shape[0]} rows, a batch {rows_max}")
     dev = _need_gpu(idx_dev, val_dev)
     rows = ctypes.c_int64(0)
     with torch.cuda.device(dev):
@@ -474,6 +503,7 @@ def kd_cache_loader_next(handle: ctypes.c_void_p, idx_dev: torch.Tensor, val_dev
 
 
 def kd_cache_loader_close(handle: ctypes.c_void_p) -> None:
+    _HANDLES.pop(handle.value if handle is not None else None, None)
     _check(load_library().kd_cache_loader_close(handle), "kd_cache_loader_close")
 
 
@@ -530,6 +560,7 @@ def kd_cache_writer_open(prefix: str, shard_tokens: int, vocab: int, k: int, val
     h = ctypes.c_void_p()
     _check(load_library().kd_cache_writer_open(os.fsencode(prefix), ctypes.byref(info), int(max_batch_tokens),
                                                int(depth), ctypes.byref(h)), "kd_cache_writer_open")
+    _HANDLES[h.value] = (int(max_batch_tokens), int(k), val_dtype)
     return h
 
 
@@ -538,9 +569,8 @@ def kd_cache_writer_put(handle: ctypes.c_void_p, idx_dev: torch.Tensor, val_dev:
     the copies run on the current stream of their device.  The tensors must stay
     unchanged until those copies have run (the next put or close waits for them
     only as far as buffer space requires)."""
+    _batch_tensors(handle, idx_dev, val_dev, "kd_cache_writer_put")
     dev = _need_gpu(idx_dev, val_dev)
-    if idx_dev.dtype != torch.int32 or idx_dev.dim() != 2 or val_dev.shape != idx_dev.shape:
-        raise ValueError("idx must be int32 [rows, K] and val [rows, K]")
     with torch.cuda.device(dev):
         _check(load_library().kd_cache_writer_put(handle, _ptr(idx_dev), _ptr(val_dev), int(idx_dev.shape[0]),
                                                   _stream(dev)), "kd_cache_writer_put")
@@ -548,6 +578,7 @@ def kd_cache_writer_put(handle: ctypes.c_void_p, idx_dev: torch.Tensor, val_dev:
 
 def kd_cache_writer_close(handle: ctypes.c_void_p) -> int:
     """Write the last shard and free the writer; returns the number of shards."""
+    _HANDLES.pop(handle.value if handle is not None else None, None)
     n = ctypes.c_int64(0)
     _check(load_library().kd_cache_writer_close(handle, ctypes.byref(n)), "kd_cache_writer_close")
     return int(n.value)
@@ -572,6 +603,7 @@ class CacheWriter:
         error is raised: the shards written before it are complete and in order."""
         if self.handle is not None:
             h, self.handle = self.handle, None
+            _HANDLES.pop(h.value, None)
             n = ctypes.c_int64(0)
             st = load_library().kd_cache_writer_close(h, ctypes.byref(n))
             self.paths = [f"{self.prefix}_{i:05d}.kdc" for i in range(n.value)]

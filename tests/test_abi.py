@@ -187,6 +187,44 @@ def test_python_binding_refuses_cpu_tensors():
         kd.kd_chunked_kl_fwd(h, w, idx, val, 1.0)
 
 
+def test_python_binding_checks_shapes_before_pointers():
+    """The library sees pointers and sizes only, so the binding refuses inputs
+    whose shapes or dtypes disagree before it takes a pointer (here on CPU tensors,
+    so the shape error comes before the no-CPU-fallback one)."""
+    import torch
+    bf = torch.bfloat16
+    h = torch.zeros(4, 8, dtype=bf)
+    idx = torch.zeros(4, 2, dtype=torch.int32)
+    val = torch.zeros(4, 2, dtype=bf)
+    lse = torch.zeros(4, dtype=torch.float32)
+    bad = [
+        (dict(w=torch.zeros(10, 16, dtype=bf)), "w \\[V, d\\]"),        # W of another hidden size
+        (dict(w=torch.zeros(10, 8, dtype=torch.float32)), "one dtype"),  # W of another dtype
+        (dict(w=torch.zeros(80, dtype=bf)), "w \\[V, d\\]"),            # W not 2-D
+        (dict(idx=torch.zeros(3, 2, dtype=torch.int32), val=torch.zeros(3, 2, dtype=bf)), "idx must be"),
+        (dict(idx=torch.zeros(4, 2, dtype=torch.int64)), "idx must be"),
+        (dict(val=torch.zeros(4, 3, dtype=bf)), "idx must be"),
+    ]
+    for kw, msg in bad:
+        a = dict(h=h, w=torch.zeros(10, 8, dtype=bf), idx=idx, val=val)
+        a.update(kw)
+        with pytest.raises(ValueError, match=msg):
+            kd.kd_chunked_kl_fwd(a["h"], a["w"], a["idx"], a["val"], 1.0)
+        with pytest.raises(ValueError, match=msg):
+            kd.kd_chunked_kl_bwd(a["h"], a["w"], a["idx"], a["val"], 1.0, lse)
+    w = torch.zeros(10, 8, dtype=bf)
+    for bad_lse in (torch.zeros(3, dtype=torch.float32), torch.zeros(4, dtype=bf), torch.zeros(4, 1)):
+        with pytest.raises(ValueError, match="lse must be"):
+            kd.kd_chunked_kl_bwd(h, w, idx, val, 1.0, bad_lse)
+    with pytest.raises(ValueError, match="h_t must be"):
+        kd.kd_topk_cache_build(h, torch.zeros(10, 16, dtype=bf), 2)
+    with pytest.raises(ValueError, match="h_t must be"):
+        kd.kd_topk_cache_build(h, torch.zeros(10, 8, dtype=torch.float32), 2)
+    # a well-formed call on CPU tensors still stops at the device check
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        kd.kd_chunked_kl_fwd(h, w, idx, val, 1.0)
+
+
 def test_empty_problem_workspace(lib):
     st, b = _ws(lib, kd.KD_OP_KL_FWD, _P(n=0))
     assert st == 0 and b > 0

@@ -70,6 +70,40 @@ def test_loader_end_and_raw_calls(tmp_path):
         kd.kd_cache_loader_close(h)
 
 
+def test_raw_calls_check_tensors_against_the_handle(tmp_path):
+    """The raw next/put calls take caller tensors: a batch of another K or value
+    dtype, or too few rows for a loader batch, is refused before any copy is
+    enqueued, and the handle keeps working."""
+    idx, val = _cache(10, 4, 100, torch.float32, 5)
+    p = str(tmp_path / "a.kdc")
+    kd.kd_cache_write(p, idx, val, 100)
+    h = kd.kd_cache_loader_open([p], 4, 2)
+    try:
+        bad = [((4, 5), torch.float32), ((4, 4), torch.bfloat16), ((3, 4), torch.float32)]
+        for shape, vdt in bad:
+            with pytest.raises(ValueError, match="kd_cache_loader_next"):
+                kd.kd_cache_loader_next(h, torch.empty(shape, dtype=torch.int32, device=DEV),
+                                        torch.empty(shape, dtype=vdt, device=DEV))
+        i_dev = torch.empty((6, 4), dtype=torch.int32, device=DEV)   # more rows than a batch is fine
+        v_dev = torch.empty((6, 4), dtype=torch.float32, device=DEV)
+        assert kd.kd_cache_loader_next(h, i_dev, v_dev) == 4
+        torch.cuda.synchronize()
+        assert torch.equal(i_dev[:4].cpu(), idx[:4])
+    finally:
+        kd.kd_cache_loader_close(h)
+    with pytest.raises(ValueError, match="not an open handle"):
+        kd.kd_cache_loader_next(h, i_dev, v_dev)
+
+    with kd.CacheWriter(str(tmp_path / "w"), 8, 100, 4, torch.float32, 6) as wr:
+        for shape, vdt in [((2, 5), torch.float32), ((2, 4), torch.bfloat16)]:
+            with pytest.raises(ValueError, match="kd_cache_writer_put"):
+                wr.put(torch.zeros(shape, dtype=torch.int32, device=DEV), torch.zeros(shape, dtype=vdt, device=DEV))
+        wr.put(idx[:6].to(DEV), val[:6].to(DEV))
+    assert len(wr.paths) == 1
+    got_i, got_v = kd.kd_cache_read(wr.paths[0])
+    assert torch.equal(got_i, idx[:6]) and torch.equal(got_v, val[:6])
+
+
 def test_loss_from_loaded_cache_is_identical(tmp_path):
     """Teacher cache built on the GPU, written to two shards, streamed back through the
     loader: the forward loss and lse are bitwise those of the cache as built."""

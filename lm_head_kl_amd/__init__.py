@@ -258,6 +258,8 @@ def kd_topk_cache_build(h_t: torch.Tensor, w_t: torch.Tensor, k: int, chunk_toke
 def _opts(labels: Optional[torch.Tensor], ignore_index: int, ce_weight: float, n: int
           ) -> Optional[KDLossOpts]:
     """The loss options, or None for the plain loss (no labels and no mix)."""
+    if not -2**31 <= int(ignore_index) < 2**31:
+        raise ValueError("ignore_index must fit in int32")
     if labels is None and ce_weight == 0.0:
         return None
     if labels is not None and (labels.dtype != torch.int32 or labels.shape != (n,)):
@@ -380,7 +382,9 @@ class ChunkedTopKKLLoss(torch.nn.Module):
 
     ``hidden`` is ``[..., d]`` (for example ``[batch, seq, d]``), ``idx`` / ``val``
     are ``[..., K]`` and ``labels`` ``[...]`` over the same leading axes; they are
-    flattened to rows as views (no copy, so they must be contiguous).  The head
+    flattened to rows as views (no copy, so they must be contiguous).  ``labels``
+    may be int32 or int64 (as for ``cross_entropy``); int64 labels are converted on
+    the device, and a value int32 cannot hold counts as out of range.  The head
     weight is ``[V, d]`` as in ``nn.Linear(d, V, bias=False).weight``.  Returns the
     mean top-K KL over the tokens (over the counted tokens with labels), mixed with
     the labels' cross-entropy when ``ce_weight`` > 0."""
@@ -402,6 +406,11 @@ class ChunkedTopKKLLoss(torch.nn.Module):
             raise ValueError("labels must have the hidden states' leading axes")
         h = hidden.view(-1, d)
         lab = None if labels is None else labels.view(-1)
+        if lab is not None and lab.dtype == torch.int64:
+            v = weight.shape[0]
+            bad = v + 1 if v == self.ignore_index else v      # out of [0, V) and not the ignore index
+            wide = (lab < -2**31) | (lab >= 2**31)
+            lab = torch.where(wide, torch.full_like(lab, bad), lab).to(torch.int32)
         return chunked_kl_loss(h, weight, idx.view(-1, k), val.view(-1, k), self.tau, self.chunk_tokens, lab,
                                self.ignore_index, self.ce_weight)
 

@@ -172,6 +172,9 @@ def test_option_errors():
         assert e.value.status == 14
     with pytest.raises(ValueError):
         kd.kd_chunked_kl_fwd(h, w, ti, tv, 1.0, labels=tl[:63].contiguous())
+    for ii in (2**31, -2**31 - 1):
+        with pytest.raises(ValueError, match="ignore_index"):
+            kd.kd_chunked_kl_fwd(h, w, ti, tv, 1.0, labels=tl, ignore_index=ii)
 
 
 def test_kd_check_reports_out_of_range_label():
@@ -228,3 +231,17 @@ def test_loss_module_over_batch_and_sequence_axes():
     assert torch.equal(h3.grad.view(-1, d), h2.grad) and torch.equal(w1.grad, w2.grad)
     with pytest.raises(ValueError):
         mod(h3, w1, ti, tv)
+    # int64 labels, as cross_entropy takes them, give the same loss bit for bit
+    l64 = mod(h3.detach(), w, ti.view(b, t, k), tv.view(b, t, k), tl.view(b, t).to(torch.int64))
+    torch.cuda.synchronize()
+    assert torch.equal(l64, ref.detach())
+    # an int64 label that int32 cannot hold is out of range (a NaN row), never wrapped
+    # onto a valid class: 2^32 + 5 would truncate to 5
+    wide = tl.view(b, t).to(torch.int64).clone()
+    wide[1, 7] = 2**32 + 5
+    lw = mod(h3.detach(), w, ti.view(b, t, k), tv.view(b, t, k), wide)
+    five = tl.view(b, t).to(torch.int64).clone()
+    five[1, 7] = 5
+    l5 = mod(h3.detach(), w, ti.view(b, t, k), tv.view(b, t, k), five)
+    torch.cuda.synchronize()
+    assert torch.isnan(lw) and torch.isfinite(l5)

@@ -47,6 +47,9 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
  *     the call returns without waiting. Two calls that share a workspace must be
  *     ordered on one stream.
+ *   - Threads: the compute calls and kd_workspace_size may be made from several
+ *     host threads at once (each call with its own workspace); the profiling hooks
+ *     below are the exception.
  *   - Outputs are overwritten, never accumulated into.
  *   - Errors: every argument error returns a non-zero kd_status BEFORE anything is
  *     enqueued or any HIP call is made; KD_ERR_NO_DEVICE / KD_ERR_UNSUPPORTED_ARCH

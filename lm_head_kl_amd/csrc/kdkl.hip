@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <atomic>
 #include <cstring>
 #include <string>
 #include <type_traits>
@@ -183,25 +184,30 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
+// Per-device answer cached for later calls.  Calls may come from several threads at
+// once: the caches are atomics (every thread that fills one stores the same value).
 kd_status check_device() {
-  static int state[256];   // 0 unknown, 1 gfx950, 2 other
+  static std::atomic<int> state[256];   // 0 unknown, 1 gfx950, 2 other
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KD_ERR_NO_DEVICE;
-  if (dev < 256 && state[dev]) return state[dev] == 1 ? KD_OK : KD_ERR_UNSUPPORTED_ARCH;
+  const int known = dev < 256 ? state[dev].load(std::memory_order_relaxed) : 0;
+  if (known) return known == 1 ? KD_OK : KD_ERR_UNSUPPORTED_ARCH;
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KD_ERR_NO_DEVICE;
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 256) state[dev] = ok ? 1 : 2;
+  if (dev < 256) state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? KD_OK : KD_ERR_UNSUPPORTED_ARCH;
 }
 
 bool debug_checks() {
-  static int v = -1;
-  if (v < 0) {
+  static std::atomic<int> v{-1};
+  int c = v.load(std::memory_order_relaxed);
+  if (c < 0) {
     const char* e = std::getenv("KD_CHECK");
-    v = (e && e[0] == '1') ? 1 : 0;
+    c = (e && e[0] == '1') ? 1 : 0;
+    v.store(c, std::memory_order_relaxed);
   }
-  return v == 1;
+  return c == 1;
 }
 
 inline kd_status launched() { return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH; }

@@ -423,20 +423,21 @@ class ChunkedTopKKLLoss(torch.nn.Module):
 
 _VAL_TORCH = {KD_F32: torch.float32, KD_BF16: torch.bfloat16}
 
-# open loader and writer handles -> (rows one call moves at most, K, value dtype), so
-# that the device tensors of next/put are checked against them before a copy is
-# enqueued (the library sees only pointers)
+# open loader and writer handles -> [rows one call moves at most, K, value dtype,
+# rows a loader has still to hand out (None for a writer)], so that the device
+# tensors of next/put are checked against them before a copy is enqueued (the
+# library sees only pointers)
 _HANDLES = {}
 
 
-def _batch_tensors(handle: ctypes.c_void_p, idx: torch.Tensor, val: torch.Tensor, where: str) -> int:
+def _batch_tensors(handle: ctypes.c_void_p, idx: torch.Tensor, val: torch.Tensor, where: str) -> list:
     spec = _HANDLES.get(handle.value if handle is not None else None)
     if spec is None:
         raise ValueError(f"{where}: not an open handle")
-    rows, k, vdt = spec
+    k, vdt = spec[1], spec[2]
     if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[1] != k or val.shape != idx.shape or val.dtype != vdt:
         raise ValueError(f"{where}: idx must be int32 [rows, {k}] and val {vdt} [rows, {k}]")
-    return rows
+    return spec
 
 
 def _host(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
@@ -485,7 +486,7 @@ def kd_cache_loader_open(paths, batch_tokens: int, prefetch: int = 2) -> ctypes.
     _check(load_library().kd_cache_loader_open(arr, len(enc), int(batch_tokens), int(prefetch), ctypes.byref(h)),
            "kd_cache_loader_open")
     info = kd_cache_loader_info(h)
-    _HANDLES[h.value] = (min(int(batch_tokens), max(info["n_tokens"], 1)), info["k"], _VAL_TORCH[info["val_dtype"]])
+    _HANDLES[h.value] = [int(batch_tokens), info["k"], _VAL_TORCH[info["val_dtype"]], info["n_tokens"]]
     return h
 
 
@@ -499,15 +500,23 @@ def kd_cache_loader_info(handle: ctypes.c_void_p) -> dict:
 def kd_cache_loader_next(handle: ctypes.c_void_p, idx_dev: torch.Tensor, val_dev: torch.Tensor) -> int:
     """Enqueue the next batch's copies into the device tensors (on the current
     stream of their device); returns its row count, 0 at the end.  The tensors
-    hold at least one batch: idx int32 [>= batch_tokens, K], val [same]."""
-    rows_max = _batch_tensors(handle, idx_dev, val_dev, "kd_cache_loader_next")
-    if idx_dev.shape[0] < rows_max:
-        raise ValueError(f"kd_cache_loader_next: the tensors hold {idx_dev.shape[0]} rows, a batch {rows_max}")
-    dev = _need_gpu(idx_dev, val_dev)
+    hold at least that batch: idx int32 [>= rows, K], val [same] (rows =
+    batch_tokens, fewer for the last batch, 0 at the end)."""
+    spec = _batch_tensors(handle, idx_dev, val_dev, "kd_cache_loader_next")
+    need = min(spec[0], spec[3])
+    if idx_dev.shape[0] < need:
+        raise ValueError(f"kd_cache_loader_next: the tensors hold {idx_dev.shape[0]} rows, the next batch {need}")
     rows = ctypes.c_int64(0)
-    with torch.cuda.device(dev):
-        _check(load_library().kd_cache_loader_next(handle, _ptr(idx_dev), _ptr(val_dev), ctypes.byref(rows),
-                                                   _stream(dev)), "kd_cache_loader_next")
+    if need > 0:
+        dev = _need_gpu(idx_dev, val_dev)
+        with torch.cuda.device(dev):
+            _check(load_library().kd_cache_loader_next(handle, _ptr(idx_dev), _ptr(val_dev), ctypes.byref(rows),
+                                                       _stream(dev)), "kd_cache_loader_next")
+    else:
+        # every row handed out: the library returns 0 rows and touches no buffer
+        _check(load_library().kd_cache_loader_next(handle, None, None, ctypes.byref(rows), None),
+               "kd_cache_loader_next")
+    spec[3] -= int(rows.value)
     return int(rows.value)
 
 
@@ -569,7 +578,7 @@ def kd_cache_writer_open(prefix: str, shard_tokens: int, vocab: int, k: int, val
     h = ctypes.c_void_p()
     _check(load_library().kd_cache_writer_open(os.fsencode(prefix), ctypes.byref(info), int(max_batch_tokens),
                                                int(depth), ctypes.byref(h)), "kd_cache_writer_open")
-    _HANDLES[h.value] = (int(max_batch_tokens), int(k), val_dtype)
+    _HANDLES[h.value] = [int(max_batch_tokens), int(k), val_dtype, None]
     return h
 
 

@@ -94,6 +94,24 @@ def test_raw_calls_check_tensors_against_the_handle(tmp_path):
     with pytest.raises(ValueError, match="not an open handle"):
         kd.kd_cache_loader_next(h, i_dev, v_dev)
 
+    # slices of one buffer, as a caller filling a whole cache does: the last batch
+    # gets a shorter slice and the end call an empty one
+    li = torch.empty((10, 4), dtype=torch.int32, device=DEV)
+    lv = torch.empty((10, 4), dtype=torch.float32, device=DEV)
+    h = kd.kd_cache_loader_open([p], 4, 2)
+    try:
+        row, got = 0, []
+        while True:
+            r = kd.kd_cache_loader_next(h, li[row:row + 4], lv[row:row + 4])
+            got.append(r)
+            if r == 0:
+                break
+            row += r
+    finally:
+        kd.kd_cache_loader_close(h)
+    torch.cuda.synchronize()
+    assert got == [4, 4, 2, 0] and torch.equal(li.cpu(), idx) and torch.equal(lv.cpu(), val)
+
     with kd.CacheWriter(str(tmp_path / "w"), 8, 100, 4, torch.float32, 6) as wr:
         for shape, vdt in [((2, 5), torch.float32), ((2, 4), torch.bfloat16)]:
             with pytest.raises(ValueError, match="kd_cache_writer_put"):

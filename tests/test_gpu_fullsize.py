@@ -140,13 +140,13 @@ def test_sweep_points(n, k):
 def test_peak_memory_linear_in_tokens():
     """Peak device memory of forward + backward grows linearly with N, with a
     slope of a few KB per token (inputs, cache and gradients), far below the
-    2 x V bytes per token an N x V bf16 logit tensor would add.  The driver's
+    2 x V bytes per token an N x V bf16 logit tensor would add.  The HIP runtime's
     used-memory count (hipMemGetInfo) moves with torch's reserved memory: no device
     memory is allocated outside the caller's allocator."""
     w = kd_synth.WORKLOADS["sweep_v128k"]
     torch.cuda.synchronize()
     free0, total0 = torch.cuda.mem_get_info()
-    driver_base = (total0 - free0) - torch.cuda.memory_reserved()   # context and other non-torch use
+    runtime_base = (total0 - free0) - torch.cuda.memory_reserved()   # context and other non-torch use
     W = to_dev(kd_synth.student_head(w), "bf16")
     Hfull = kd_synth.hidden(w, 131072)
     peaks = {}
@@ -163,10 +163,10 @@ def test_peak_memory_linear_in_tokens():
         torch.cuda.synchronize()
         peaks[n] = torch.cuda.max_memory_allocated() - base + (h.numel() * 2 + idx.size * 6)
         del loss, lse, dh, dw, h, ti, tv
-    # the driver's view agrees with torch's: the library allocates no device memory
+    # the runtime's view agrees with torch's: the library allocates no device memory
     # of its own (everything, workspace included, comes through the caching allocator)
     free, total = torch.cuda.mem_get_info()
-    assert (total - free) - torch.cuda.memory_reserved() - driver_base < 256 << 20
+    assert (total - free) - torch.cuda.memory_reserved() - runtime_base < 256 << 20
     ns = np.array(sorted(peaks), dtype=np.float64)
     ps = np.array([peaks[int(x)] for x in ns])
     b, a = np.polyfit(ns, ps, 1)

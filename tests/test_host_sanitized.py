@@ -12,8 +12,15 @@ The sanitizers apply to host code only; no device code is built or run here.
   past every domain limit, checked against the header's domain, and the argument
   errors of every entry point, none of which reaches the device.
 
-Any invalid memory access, leak or undefined operation (signed overflow in the
-size arithmetic included) makes a program fail.
+* kdcache.cpp again, with tests/c_abi/hip_host_stub.cpp in place of the HIP
+  runtime (host memory for pinned and device buffers, copies at once), so that
+  the writer's and loader's background threads run here: under ThreadSanitizer,
+  then AddressSanitizer, driven by tests/c_abi/kdcache_threads.c (uneven batches
+  into shards, loading across shard boundaries, the writer's failure path, a
+  loader closed mid-stream, four writer/loader pairs at once).
+
+Any invalid memory access, leak, data race or undefined operation (signed
+overflow in the size arithmetic included) makes a program fail.
 """
 import os
 import shutil
@@ -81,3 +88,24 @@ def test_loss_library_host_code_under_sanitizers(tmp_path):
     _run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", *SAN, *inc, "-c",
           os.path.join(ROOT, "tests", "c_abi", "kdkl_check.c"), "-o", drv])
     assert _link_and_run(tmp_path, [drv, lib], []) > 1_000_000
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or shutil.which("gcc") is None, reason="needs gcc and g++")
+@pytest.mark.parametrize("san", ["thread", "address,undefined"])
+def test_cache_threads_under_sanitizers(tmp_path, san):
+    inc = ["-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include")]
+    flags = [f"-fsanitize={san}", "-fno-omit-frame-pointer", "-g", "-O1", "-Wall", "-Wextra", "-Werror"]
+    objs = []
+    for src, cc, std in ((os.path.join("lm_head_kl_amd", "csrc", "kdcache.cpp"), "g++", "c++17"),
+                         (os.path.join("tests", "c_abi", "hip_host_stub.cpp"), "g++", "c++17"),
+                         (os.path.join("tests", "c_abi", "kdcache_threads.c"), "gcc", "c11")):
+        obj = os.path.join(tmp_path, os.path.basename(src) + ".o")
+        _run([cc, f"-std={std}", *flags, *inc, "-c", os.path.join(ROOT, src), "-o", obj])
+        objs.append(obj)
+    exe = os.path.join(tmp_path, "threads")
+    _run(["g++", f"-fsanitize={san}", *objs, "-lpthread", "-o", exe])
+    scratch = tmp_path / "scratch"
+    scratch.mkdir()
+    env = dict(ENV, TSAN_OPTIONS="halt_on_error=1:second_deadlock_stack=1")
+    out = _run([exe, str(scratch)], env=env, timeout=300)
+    assert out.strip().startswith("ok "), out

@@ -32,7 +32,6 @@ brute force and finite differences.  No function here
 is "parity unpinned".
 """
 from .kl import (  # noqa: F401
-    student_logits,
     logsumexp_rows,
     teacher_probs,
     kl_forward,

@@ -39,11 +39,6 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def student_logits(H, W) -> np.ndarray:
-    """``Z = H @ W^T`` in float64 (the LM-head projection)."""
-    return _f64(H) @ _f64(W).T
-
-
 def logsumexp_rows(Z) -> np.ndarray:
     """``log sum_v exp(Z[i, v])`` per row, shifted by the row max for range."""
     Z = _f64(Z)

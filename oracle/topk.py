@@ -54,11 +54,6 @@ def bf16_bits(values_exact) -> np.ndarray:
     return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
-def teacher_scores(H_T, W_T) -> np.ndarray:
-    """Teacher logits ``S = H_T @ W_T^T`` in float64."""
-    return np.asarray(H_T, np.float64) @ np.asarray(W_T, np.float64).T
-
-
 def topk_cache(H_T, W_T, k: int, val_dtype: str = "bf16", block: int = 256
                ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Exact per-row top-K of the teacher logits.

@@ -55,6 +55,70 @@ def traffic_for(kind: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi, every 25 ms) in a background thread
+    between start() and stop(); stop() returns the mean in MHz, or None when the
+    clock cannot be read (no amdsmi, or not exactly one GPU visible to it)."""
+
+    def __init__(self):
+        self.samples = []
+        self.handle = None
+        self._stop = None
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if len(hs) == 1:
+                self.handle = hs[0]
+                self._amdsmi = amdsmi
+                self._read()
+        except Exception:
+            self.handle = None
+
+    def _read(self):
+        c = self._amdsmi.amdsmi_get_clock_info(self.handle, self._amdsmi.AmdSmiClkType.GFX)
+        return float(c["clk"])
+
+    def _run(self):
+        import time as _t
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                pass
+            _t.sleep(0.025)
+
+    def start(self):
+        if self.handle is None:
+            return
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self.handle is None or self._thread is None:
+            return None
+        self._stop.set()
+        self._thread.join()
+        self._thread = None
+        s = [x for x in self.samples if x > 0]
+        return (sum(s) / len(s), len(s)) if s else None
+
+
 def cpu_baseline(workload, n_rows: int, k: int):
     """The float64 oracle, as it stands, on the first ``n_rows`` tokens of the same
     workload (full vocabulary and hidden size) with a synthetic cache of the same
@@ -62,9 +126,13 @@ def cpu_baseline(workload, n_rows: int, k: int):
     import numpy as np
     import kd_synth
     import oracle
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in libs] or [1])
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')} ({libs[0].get('threading_layer')})"
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     H = kd_synth.to_float64(kd_synth.hidden(workload, n_rows), workload.dtype)
@@ -76,6 +144,7 @@ def cpu_baseline(workload, n_rows: int, k: int):
     oracle.kl_backward(H, W, idx, val, workload.tau)
     dt = time.perf_counter() - t0
     return {"value": n_rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": host_cpu_model(), "blas": blas, "numpy": np.__version__,
             "sample": f"first {n_rows} tokens of the workload (full V={workload.vocab}, d={workload.d}, K={k}), "
                       f"float64 forward+backward, synthetic cache of the same shape; {dt:.1f} s"}
 
@@ -315,6 +384,123 @@ def variants(kd, torch, h, wd, idx, val, w, dh_dtype, steps, chunk, ce_weight=0.
             "options": f"labels over V, last 1/{round(1 / pad_frac)} of every {seq}-token sequence ignored"}
 
 
+def inputs_and_cache(kd, torch, np, kd_synth, w, n, k, dev, timed=True):
+    """Device inputs of workload ``w`` (first n tokens) and its teacher cache, built
+    with kd_topk_cache_build (H_T = H: the synthetic teacher shares the hidden
+    states); the second build is timed."""
+    def to_dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    t0 = time.perf_counter()
+    h = to_dev(kd_synth.hidden(w, n))
+    wd = to_dev(kd_synth.student_head(w))
+    wt = to_dev(kd_synth.teacher_head(w))
+    torch.cuda.synchronize()
+    log(f"{w.name}: N={n} d={w.d} V={w.vocab} K={k} tau={w.tau} {w.dtype}; inputs in "
+        f"{time.perf_counter() - t0:.1f}s")
+    idx, val = kd.kd_topk_cache_build(h, wt, k)
+    torch.cuda.synchronize()
+    cache = None
+    if timed:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        idx, val = kd.kd_topk_cache_build(h, wt, k)
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1)
+        cache = {"ms": round(cms, 3), "tokens_per_s": n / (cms / 1e3),
+                 "mfma_frac": 2.0 * n * w.vocab * w.d / (cms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)}
+        log(f"cache build {cms:.1f} ms ({cache['tokens_per_s']:.0f} tokens/s)")
+    del wt
+    return h, wd, idx, val, cache
+
+
+def measure(kd, torch, w, h, wd, idx, val, n, k, steps, warmup, chunk, clock):
+    """`warmup` untimed and `steps` timed fwd+bwd steps.  Whole-run wall time gives
+    tokens/s; HIP events on the launch stream give each step's time (median, min)
+    and, through the library's profiling hooks, each kernel's average launch time
+    (the roofline of the dominant kernel).  The graphics clock is sampled meanwhile."""
+    dev = h.device
+    dh_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def step():
+        loss, lse, _ = kd.kd_chunked_kl_fwd(h, wd, idx, val, w.tau, chunk_tokens=chunk)
+        dh, dw = kd.kd_chunked_kl_bwd(h, wd, idx, val, w.tau, lse, None, dh_dtype=dh_dtype, chunk_tokens=chunk)
+        return loss, dh, dw
+
+    for i in range(warmup):
+        wl = step()[0].item()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{warmup} loss={wl:.5f}")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    kd.profile_begin()
+    clock.start()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    out = None
+    ev[0].record()
+    for i in range(steps):
+        out = None          # a training loop has consumed the previous step's gradients
+        out = step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    clk = clock.stop()
+    stats = kd.profile_end()
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    # peak of the step: what it allocates (outputs, workspace) on top of the resident
+    # inputs (H, W, cache), counted in full
+    own = sum(t.numel() * t.element_size() for t in (h, wd, idx, val))
+    peak_gb = (torch.cuda.max_memory_allocated(dev) - base + own) / 1e9
+    loss_val = out[0].item()
+    del out
+    ms = t_total * 1e3 / steps
+    flops_step = 8.0 * n * w.vocab * w.d
+    peak_tf = BF16_DENSE_PEAK_TFLOPS if w.dtype == "bf16" else FP32_DENSE_PEAK_TFLOPS
+    mfma_util = flops_step / (ms / 1e3) / (peak_tf * 1e12)
+    mid = per_step[len(per_step) // 2] if steps % 2 else 0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2])
+    clock_mhz = None if clk is None else round(clk[0], 1)
+    # utilisation against the peak at the clock measured meanwhile (the peak scales with it)
+    util_clk = None if clk is None else round(mfma_util * 2400.0 / clk[0], 4)
+    log(f"{steps} steps: {ms:.2f} ms/step (median {mid:.2f}, min {per_step[0]:.2f}), {n / (ms / 1e3):.0f} tokens/s, "
+        f"MFMA {100 * mfma_util:.1f}% of dense peak at 2.4 GHz"
+        + (f", {100 * util_clk:.1f}% at the measured {clock_mhz:.0f} MHz ({clk[1]} samples)" if clk else "")
+        + f", peak {peak_gb:.2f} GB, loss={loss_val:.5f}")
+    tot = sum(v["total_ms"] for v in stats.values())
+    for kind, st in sorted(stats.items(), key=lambda kv: -kv[1]["total_ms"]):
+        avg = st["total_ms"] / max(1, st["launches"])
+        tf = st["flops"] / (st["total_ms"] / 1e3) / 1e12 if st["flops"] and st["total_ms"] else 0.0
+        gbs = st["bytes"] / (st["total_ms"] / 1e3) / 1e9 if st["total_ms"] else 0.0
+        log(f"  {kind:14s} {st['launches']:5d} launches  {st['total_ms'] / steps:9.3f} ms/step "
+            f"({100 * st['total_ms'] / tot:5.1f}%)  avg {avg:8.3f} ms  {tf:7.1f} TFLOP/s  {gbs:7.1f} GB/s")
+    dom_kind, dom = max(stats.items(), key=lambda kv: kv[1]["total_ms"])
+    avg_s = dom["total_ms"] / dom["launches"] / 1e3
+    per_launch_flops = dom["flops"] / dom["launches"]
+    if per_launch_flops > 0:
+        achieved = per_launch_flops / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_tf, 4), "traffic": traffic_for(dom_kind), "kernel": dom_kind,
+                "avg_launch_ms": round(avg_s * 1e3, 4), "flops_per_launch": per_launch_flops}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom_kind), "kernel": dom_kind,
+                "avg_launch_ms": round(avg_s * 1e3, 4)}
+    return {"workload": w.name, "n_tokens": n, "d": w.d, "vocab": w.vocab, "k": k, "tau": w.tau,
+            "tokens_per_s": round(n / (ms / 1e3), 1), "ms_per_step": round(ms, 3), "ms_median": round(mid, 3),
+            "ms_min": round(per_step[0], 3), "mfma_util": round(mfma_util, 4),
+            "mfma_util_measured_clock": util_clk, "clock_mhz": clock_mhz, "peak_gb": round(peak_gb, 3),
+            "loss": round(loss_val, 5), "roofline": roof,
+            "kernels_ms_per_step": {k2: round(v["total_ms"] / steps, 4) for k2, v in stats.items()},
+            "_stats": stats}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,6 +515,8 @@ def main() -> int:
     ap.add_argument("--no-cache-build-timing", action="store_true")
     ap.add_argument("--no-cache-io", action="store_true",
                     help="skip writing the cache to shards and streaming it back with the loader")
+    ap.add_argument("--no-target-point", action="store_true",
+                    help="skip timing the 32,768-token point (V=128,256, d=4,096, K=100) after the main workload")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the step with the loss options (padding mask, cross-entropy mix)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -365,6 +553,7 @@ def main() -> int:
     if args.sweep:
         return sweep(kd, torch, np, kd_synth, max(1, args.steps), args.warmup)
     dev = torch.device("cuda:0")
+    clock = ClockSampler()
     w = kd_synth.WORKLOADS[args.workload]
     n = args.tokens or w.tokens[0]
     k = args.k or (100 if 100 in w.ks else w.ks[0])
@@ -375,84 +564,14 @@ def main() -> int:
             return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(x).to(dev)
 
-    t0 = time.perf_counter()
-    h = to_dev(kd_synth.hidden(w, n))
-    wd = to_dev(kd_synth.student_head(w))
-    wt = to_dev(kd_synth.teacher_head(w))
-    torch.cuda.synchronize()
-    log(f"{args.workload}: N={n} d={w.d} V={w.vocab} K={k} tau={w.tau} {w.dtype}; inputs in "
-        f"{time.perf_counter() - t0:.1f}s")
-
-    # offline teacher cache (H_T = H: the synthetic teacher shares the hidden states)
-    idx, val = kd.kd_topk_cache_build(h, wt, k)
-    torch.cuda.synchronize()
-    cache = None
-    if not args.no_cache_build_timing:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        idx, val = kd.kd_topk_cache_build(h, wt, k)
-        e1.record()
-        torch.cuda.synchronize()
-        cms = e0.elapsed_time(e1)
-        cache = {"ms": round(cms, 3), "tokens_per_s": n / (cms / 1e3),
-                 "mfma_frac": 2.0 * n * w.vocab * w.d / (cms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)}
-        log(f"cache build {cms:.1f} ms ({cache['tokens_per_s']:.0f} tokens/s)")
-    del wt
-
+    h, wd, idx, val, cache = inputs_and_cache(kd, torch, np, kd_synth, w, n, k, dev,
+                                              timed=not args.no_cache_build_timing)
     dh_dtype = tdt
-
-    def step():
-        loss, lse, _ = kd.kd_chunked_kl_fwd(h, wd, idx, val, w.tau, chunk_tokens=args.chunk)
-        dh, dw = kd.kd_chunked_kl_bwd(h, wd, idx, val, w.tau, lse, None, dh_dtype=dh_dtype, chunk_tokens=args.chunk)
-        return loss, dh, dw
-
-    for i in range(args.warmup):
-        wl = step()[0].item()
-        torch.cuda.synchronize()
-        log(f"warmup {i + 1}/{args.warmup} loss={wl:.5f}")
-    torch.cuda.synchronize()
-    torch.cuda.reset_peak_memory_stats(dev)
-    kd.profile_begin()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    out = None
-    for i in range(args.steps):
-        out = None          # a training loop has consumed the previous step's gradients
-        out = step()
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
-    stats = kd.profile_end()
-    peak_gb = torch.cuda.max_memory_allocated(dev) / 1e9
-    loss_val = out[0].item()
-    del out
-    ms = t_total * 1e3 / args.steps
-    value = n / (t_total / args.steps)
-    flops_step = 8.0 * n * w.vocab * w.d
-    peak_tf = BF16_DENSE_PEAK_TFLOPS if w.dtype == "bf16" else FP32_DENSE_PEAK_TFLOPS
-    mfma_util = flops_step / (ms / 1e3) / (peak_tf * 1e12)
-    log(f"{args.steps} steps: {ms:.2f} ms/step, {value:.0f} tokens/s, MFMA {100 * mfma_util:.1f}% of dense peak, "
-        f"peak {peak_gb:.2f} GB, loss={loss_val:.5f}")
-    tot = sum(s["total_ms"] for s in stats.values())
-    for kind, s in sorted(stats.items(), key=lambda kv: -kv[1]["total_ms"]):
-        avg = s["total_ms"] / max(1, s["launches"])
-        tf = s["flops"] / (s["total_ms"] / 1e3) / 1e12 if s["flops"] and s["total_ms"] else 0.0
-        gbs = s["bytes"] / (s["total_ms"] / 1e3) / 1e9 if s["total_ms"] else 0.0
-        log(f"  {kind:14s} {s['launches']:5d} launches  {s['total_ms'] / args.steps:9.3f} ms/step "
-            f"({100 * s['total_ms'] / tot:5.1f}%)  avg {avg:8.3f} ms  {tf:7.1f} TFLOP/s  {gbs:7.1f} GB/s")
-
-    dom_kind, dom = max(stats.items(), key=lambda kv: kv[1]["total_ms"])
-    avg_s = dom["total_ms"] / dom["launches"] / 1e3
-    per_launch_flops = dom["flops"] / dom["launches"]
-    if per_launch_flops > 0:
-        achieved = per_launch_flops / avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tf, "unit": "TFLOP/s",
-                "frac": round(achieved / peak_tf, 4), "traffic": traffic_for(dom_kind), "kernel": dom_kind,
-                "avg_launch_ms": round(avg_s * 1e3, 4), "flops_per_launch": per_launch_flops}
-    else:
-        achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom_kind), "kernel": dom_kind,
-                "avg_launch_ms": round(avg_s * 1e3, 4)}
+    main_pt = measure(kd, torch, w, h, wd, idx, val, n, k, args.steps, args.warmup, args.chunk, clock)
+    ms, value, mfma_util, peak_gb = (main_pt["ms_per_step"], main_pt["tokens_per_s"], main_pt["mfma_util"],
+                                     main_pt["peak_gb"])
+    roof = main_pt["roofline"]
+    stats = main_pt["_stats"]
 
     var = None
     if not args.no_variants:
@@ -478,6 +597,21 @@ def main() -> int:
             f"(open {cp['open_ms']:.1f} ms, build and copies {cp['gpu_ms']:.1f} ms, last shard {cp['close_ms']:.1f} ms), "
             f"{cp['shards']} shards, {cp['bytes'] / 1e6:.1f} MB")
 
+    target = None
+    if not args.no_target_point and (args.workload, n, k) != ("ctx32k_v128k", 32768, 100):
+        # the point at which the fused loss is asked to reach half of the MFMA peak:
+        # one 32,768-token sequence at V = 128,256, d = 4,096, K = 100
+        del h, wd, idx, val
+        torch.cuda.empty_cache()
+        wt_ = kd_synth.WORKLOADS["ctx32k_v128k"]
+        h, wd, idx, val, tcache = inputs_and_cache(kd, torch, np, kd_synth, wt_, 32768, 100, dev, timed=True)
+        target = measure(kd, torch, wt_, h, wd, idx, val, 32768, 100, args.steps, args.warmup, args.chunk, clock)
+        target.pop("_stats")
+        target["cache_build"] = tcache
+        log(f"target point ctx32k_v128k: {target['tokens_per_s']:.0f} tokens/s, median {target['ms_median']:.2f} ms, "
+            f"MFMA {100 * target['mfma_util']:.1f}% (at the measured clock {target['mfma_util_measured_clock']}), "
+            f"peak {target['peak_gb']:.2f} GB")
+
     cpu = None
     if not args.no_cpu_baseline:
         del h, wd, idx, val
@@ -493,7 +627,10 @@ def main() -> int:
         "config": {"workload": args.workload, "n_tokens": n, "d": w.d, "vocab": w.vocab, "k": k, "tau": w.tau,
                    "chunk_tokens": args.chunk or "default", "teacher": w.teacher},
         "mfma_util": round(mfma_util, 4), "peak_gb": round(peak_gb, 3),
-        "roofline": roof, "cpu_baseline": cpu, "cache_build": cache, "cache_io": cio, "loss_options": var,
+        "ms_median": main_pt["ms_median"], "ms_min": main_pt["ms_min"],
+        "clock_mhz": main_pt["clock_mhz"], "mfma_util_measured_clock": main_pt["mfma_util_measured_clock"],
+        "roofline": roof, "cpu_baseline": cpu, "target_point": target, "cache_build": cache, "cache_io": cio,
+        "loss_options": var,
         "kernels_ms_per_step": {k2: round(s["total_ms"] / args.steps, 4) for k2, s in stats.items()},
     }
     print(json.dumps(line), flush=True)

@@ -40,10 +40,13 @@
  * Conventions for every call:
  *   - All data pointers are DEVICE pointers into contiguous row-major buffers,
  *     16-byte aligned. The caller owns every buffer; the library allocates no
- *     device memory and keeps no state besides a per-device architecture check.
+ *     device memory and keeps no state besides a per-device architecture check
+ *     and, for kd_chunked_kl_fwd_noalloc, a fixed scratch array per device and
+ *     its address.
  *   - Scratch memory is the caller's workspace `ws` of at least
  *     kd_workspace_size() bytes (16-byte aligned); its contents on entry do not
- *     matter and are clobbered.
+ *     matter and are clobbered (kd_chunked_kl_fwd_noalloc uses the library's
+ *     scratch array instead).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
  *     the call returns without waiting. Two calls that share a workspace must be
  *     ordered on one stream.
@@ -97,7 +100,8 @@ typedef enum {
   KD_ERR_TOPK_OVERFLOW = 11,     /* only with KD_CHECK=1: too many near-ties at the K-th value */
   KD_ERR_IO = 12,                /* kdcache.h: a file could not be opened, read or written */
   KD_ERR_BAD_FORMAT = 13,        /* kdcache.h: a shard header or file size does not match the format */
-  KD_ERR_BAD_OPTION = 14         /* a kd_loss_opts field is outside its domain */
+  KD_ERR_BAD_OPTION = 14,        /* a kd_loss_opts field is outside its domain */
+  KD_ERR_SCRATCH_TOO_SMALL = 15  /* kd_chunked_kl_fwd_noalloc: the problem needs more than the 64 MiB scratch */
 } kd_status;
 
 typedef enum { KD_OP_TOPK_BUILD = 0, KD_OP_KL_FWD = 1, KD_OP_KL_BWD = 2 } kd_op;
@@ -203,6 +207,29 @@ kd_status kd_chunked_kl_bwd_ex(const kd_problem* p, const kd_loss_opts* opts, co
                                const float* lse, const float* grad_loss,
                                void* dh_out, float* dw_out,
                                void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Allocation-free forward, for callers that cannot allocate memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * kd_chunked_kl_fwd_ex (opts may be NULL for the plain loss) whose workspace is a
+ * fixed 64 MiB scratch array inside the library (a device global, one per device,
+ * held from module load until the process ends) instead of a caller's buffer.  It
+ * calls no allocator.  Results are bitwise those of kd_chunked_kl_fwd_ex: the
+ * forward's results do not depend on the chunk.
+ *   - Chunk: p->chunk_tokens if > 0, else the largest multiple of 256 tokens up to
+ *     the library default whose workspace fits 64 MiB.  The workspace is
+ *     kd_workspace_size(KD_OP_KL_FWD, ...) at that chunk: about 4.9 KB per chunk
+ *     token at V = 128,256, K = 100 (a 13,824-token chunk), plus 0.5 byte per token
+ *     of N.  KD_ERR_SCRATCH_TOO_SMALL when the given chunk, or every chunk down to
+ *     256 tokens, needs more than 64 MiB (large V, large K or very large N).
+ *   - Every call on one device uses that device's single scratch array, and a call
+ *     leaves its contents behind.  Calls that overlap in time on one device (on
+ *     different streams or from different host threads without ordering) race on
+ *     it: order them on one stream, or synchronise between them.
+ *   - The first call on a device looks up that device's scratch address (with the
+ *     device current); later calls reuse it.  Other errors as kd_chunked_kl_fwd_ex. */
+kd_status kd_chunked_kl_fwd_noalloc(const kd_problem* p, const kd_loss_opts* opts, const void* h, const void* w,
+                                    const int32_t* idx, const void* val,
+                                    float* loss_out, float* lse_out, float* rows_out, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* kd_status_string(kd_status s);

@@ -45,12 +45,12 @@ STATUS_NAMES = {
     0: "KD_OK", 1: "KD_ERR_NULL_POINTER", 2: "KD_ERR_BAD_SHAPE", 3: "KD_ERR_BAD_DTYPE", 4: "KD_ERR_BAD_TAU",
     5: "KD_ERR_MISALIGNED", 6: "KD_ERR_WORKSPACE_TOO_SMALL", 7: "KD_ERR_NO_DEVICE", 8: "KD_ERR_UNSUPPORTED_ARCH",
     9: "KD_ERR_LAUNCH", 10: "KD_ERR_IDX_OUT_OF_RANGE", 11: "KD_ERR_TOPK_OVERFLOW", 12: "KD_ERR_IO",
-    13: "KD_ERR_BAD_FORMAT", 14: "KD_ERR_BAD_OPTION",
+    13: "KD_ERR_BAD_FORMAT", 14: "KD_ERR_BAD_OPTION", 15: "KD_ERR_SCRATCH_TOO_SMALL",
 }
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTED = ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd",
-            "kd_chunked_kl_fwd_ex", "kd_chunked_kl_bwd_ex", "kd_status_string", "kd_version", "kd_profile_begin", "kd_profile_end",
+            "kd_chunked_kl_fwd_ex", "kd_chunked_kl_bwd_ex", "kd_chunked_kl_fwd_noalloc", "kd_status_string", "kd_version", "kd_profile_begin", "kd_profile_end",
             "kd_cache_write", "kd_cache_info_read", "kd_cache_read", "kd_cache_loader_open",
             "kd_cache_loader_info", "kd_cache_loader_next", "kd_cache_loader_close",
             "kd_cache_writer_open", "kd_cache_writer_put", "kd_cache_writer_close")
@@ -129,8 +129,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     O = ctypes.POINTER(KDLossOpts)
     lib.kd_chunked_kl_fwd_ex.argtypes = [P, O, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_chunked_kl_bwd_ex.argtypes = [P, O, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_chunked_kl_fwd_noalloc.argtypes = [P, O, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in ("kd_workspace_size", "kd_topk_cache_build", "kd_chunked_kl_fwd", "kd_chunked_kl_bwd",
-              "kd_chunked_kl_fwd_ex", "kd_chunked_kl_bwd_ex"):
+              "kd_chunked_kl_fwd_ex", "kd_chunked_kl_bwd_ex", "kd_chunked_kl_fwd_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
@@ -295,6 +296,26 @@ def kd_chunked_kl_fwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: 
                                             _ptr(val), _ptr(loss), _ptr(lse), _ptr(rows), _ptr(ws), ws.numel(),
                                             _stream(dev)), "kd_chunked_kl_fwd_ex")
     return loss, lse, rows
+
+
+def kd_chunked_kl_fwd_noalloc(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, tau: float,
+                              loss: torch.Tensor, lse: torch.Tensor, rows: Optional[torch.Tensor] = None,
+                              chunk_tokens: int = 0, labels: Optional[torch.Tensor] = None,
+                              ignore_index: int = -100, ce_weight: float = 0.0) -> None:
+    """The forward into caller-provided outputs (``loss`` float32 scalar, ``lse``
+    float32 [N], ``rows`` float32 [N] or None), with the library's fixed scratch
+    array as workspace: nothing is allocated, by the library or here."""
+    n, d, v, k = _loss_inputs(h, w, idx, val, lse)
+    dev = _need_gpu(h, w, idx, val, loss, lse, rows, labels)
+    if loss.dtype != torch.float32 or loss.numel() != 1 or (rows is not None and (rows.dtype != torch.float32
+                                                                                   or rows.shape != (n,))):
+        raise ValueError("loss must be a float32 scalar and rows float32 [N]")
+    prob = make_problem(n, d, v, k, tau, _dt(h.dtype), _dt(val.dtype), KD_F32, chunk_tokens)
+    opts = _opts(labels, ignore_index, ce_weight, n)
+    with torch.cuda.device(dev):
+        _check(load_library().kd_chunked_kl_fwd_noalloc(ctypes.byref(prob), None if opts is None else ctypes.byref(opts),
+                                                         _ptr(h), _ptr(w), _ptr(idx), _ptr(val), _ptr(loss), _ptr(lse),
+                                                         _ptr(rows), _stream(dev)), "kd_chunked_kl_fwd_noalloc")
 
 
 def kd_chunked_kl_bwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, tau: float,

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <atomic>
+#include <mutex>
 #include <cstring>
 #include <string>
 #include <type_traits>
@@ -670,9 +671,73 @@ kd_status bwd_entry(const kd_problem* p, const kd_loss_opts* opts, const void* h
   return bwd_impl<float>(pl, L, h, w, idx, val, lse, grad_loss, dh_out, dw_out, (char*)ws, st, o);
 }
 
+// ---- the allocation-free forward (kd_chunked_kl_fwd_noalloc)
+//
+// Its workspace is this file-scope device array: every device the library runs on
+// holds its own copy from module load until the process ends.  In host code the
+// name `scratch` is only a host-side stand-in; the device address of each device's
+// copy comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[256];   // per device; set once under g_scratch_mu
+
+kd_status scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KD_ERR_NO_DEVICE;
+  if (dev >= 256) return KD_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KD_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return KD_OK;
+}
+
+// The forward plan whose workspace fits the scratch array: the caller's chunk when
+// one is given, else the largest multiple of 256 tokens up to the library default
+// (the forward's results do not depend on the chunk).  KD_ERR_SCRATCH_TOO_SMALL
+// when none fits.
+kd_status noalloc_plan(const kd_problem* p, Plan* pl, Layout* L) {
+  KD_TRY(validate(KD_OP_KL_FWD, p, pl));
+  if (layout(KD_OP_KL_FWD, *pl, L) <= kScratchBytes) return KD_OK;
+  if (p->chunk_tokens > 0) return KD_ERR_SCRATCH_TOO_SMALL;
+  for (int64_t c = pl->Nc - BX; c >= BX; c -= BX) {
+    pl->Nc = c;
+    pl->ld_t = pad_ld(c, pl->esz);
+    if (layout(KD_OP_KL_FWD, *pl, L) <= kScratchBytes) return KD_OK;
+  }
+  return KD_ERR_SCRATCH_TOO_SMALL;
+}
+
 }  // namespace
 
 extern "C" {
+
+kd_status kd_chunked_kl_fwd_noalloc(const kd_problem* p, const kd_loss_opts* opts, const void* h, const void* w,
+                                    const int32_t* idx, const void* val, float* loss_out, float* lse_out,
+                                    float* rows_out, void* stream) {
+  Plan pl;
+  Layout L;
+  KD_TRY(noalloc_plan(p, &pl, &L));
+  Opts o;
+  KD_TRY(read_opts(p, opts, &o));
+  if (!w || !loss_out) return KD_ERR_NULL_POINTER;
+  if (pl.N > 0 && (!h || !idx || !val || !lse_out)) return KD_ERR_NULL_POINTER;
+  if (!aligned16(h) || !aligned16(w) || !aligned16(idx) || !aligned16(val) || !aligned16(loss_out) ||
+      !aligned16(lse_out) || !aligned16(rows_out))
+    return KD_ERR_MISALIGNED;
+  KD_TRY(check_device());
+  char* ws = nullptr;
+  KD_TRY(scratch_of_current_device(&ws));
+  hipStream_t st = (hipStream_t)stream;
+  if (pl.xdt == KD_BF16) return fwd_impl<bf16_t>(pl, L, h, w, idx, val, loss_out, lse_out, rows_out, ws, st, o);
+  return fwd_impl<float>(pl, L, h, w, idx, val, loss_out, lse_out, rows_out, ws, st, o);
+}
 
 kd_status kd_chunked_kl_fwd(const kd_problem* p, const void* h, const void* w, const int32_t* idx,
                             const void* val, float* loss_out, float* lse_out, float* kl_rows_out, void* ws,
@@ -715,6 +780,7 @@ const char* kd_status_string(kd_status s_in) {
     case KD_ERR_IO: return "a cache file could not be opened, read or written";
     case KD_ERR_BAD_FORMAT: return "a cache shard does not match the shard format";
     case KD_ERR_BAD_OPTION: return "a loss option is outside its domain";
+    case KD_ERR_SCRATCH_TOO_SMALL: return "the problem needs more than the library's 64 MiB scratch array";
   }
   return "unknown status";
 }

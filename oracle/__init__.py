@@ -39,4 +39,4 @@ from .kl import (  # noqa: F401
     kl_dense_reconstruction,
 )
 from .topk import topk_cache, round_to_bf16, bf16_bits  # noqa: F401
-from .variants import counted_rows, variant_forward, variant_backward  # noqa: F401
+from .variants import counted_rows, variant_forward, variant_backward, renorm_forward, renorm_backward  # noqa: F401

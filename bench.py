@@ -379,9 +379,30 @@ def variants(kd, torch, h, wd, idx, val, w, dh_dtype, steps, chunk, ce_weight=0.
     ms = (time.perf_counter() - t0) * 1e3 / steps
     loss = out[0].item()
     del out
-    return {"tokens_per_s": n / (ms / 1e3), "ms_per_step": round(ms, 3), "ce_weight": ce_weight,
-            "ignored_frac": round(ignored, 4), "loss": round(loss, 5),
-            "options": f"labels over V, last 1/{round(1 / pad_frac)} of every {seq}-token sequence ignored"}
+    out = {"tokens_per_s": n / (ms / 1e3), "ms_per_step": round(ms, 3), "ce_weight": ce_weight,
+           "ignored_frac": round(ignored, 4), "loss": round(loss, 5),
+           "options": f"labels over V, last 1/{round(1 / pad_frac)} of every {seq}-token sequence ignored"}
+
+    # the student renormalised over the cached entries (no mix), same mask
+    def rstep():
+        loss, lse, _ = kd.kd_chunked_kl_fwd(h, wd, idx, val, w.tau, chunk_tokens=chunk, labels=lab,
+                                            student="renorm")
+        dh, dw = kd.kd_chunked_kl_bwd(h, wd, idx, val, w.tau, lse, None, dh_dtype=dh_dtype, chunk_tokens=chunk,
+                                      labels=lab, student="renorm")
+        return loss, dh, dw
+
+    rstep()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r = None
+        r = rstep()
+    torch.cuda.synchronize()
+    rms = (time.perf_counter() - t0) * 1e3 / steps
+    out["student_renorm"] = {"tokens_per_s": n / (rms / 1e3), "ms_per_step": round(rms, 3),
+                             "loss": round(r[0].item(), 5)}
+    del r
+    return out
 
 
 def inputs_and_cache(kd, torch, np, kd_synth, w, n, k, dev, timed=True):
@@ -577,7 +598,8 @@ def main() -> int:
     if not args.no_variants:
         var = variants(kd, torch, h, wd, idx, val, w, dh_dtype, max(1, min(args.steps, 3)), args.chunk)
         log(f"loss options (mask {100 * var['ignored_frac']:.2f} % of tokens, CE weight {var['ce_weight']}): "
-            f"{var['ms_per_step']:.2f} ms/step, {var['tokens_per_s']:.0f} tokens/s")
+            f"{var['ms_per_step']:.2f} ms/step, {var['tokens_per_s']:.0f} tokens/s; renormalised student: "
+            f"{var['student_renorm']['ms_per_step']:.2f} ms/step, {var['student_renorm']['tokens_per_s']:.0f} tokens/s")
 
     cio = None
     if not args.no_cache_io:

@@ -183,11 +183,24 @@ kd_status kd_chunked_kl_bwd(const kd_problem* p, const void* h, const void* w,
  * An ignored row's cache entries (idx, val) are not read, so padding may hold
  * anything there; its lse is still computed. With a = 0 the labels only mask.
  * With a > 0, a label outside [0, V) other than ignore_index makes its row's
- * term NaN (KD_CHECK=1: KD_ERR_IDX_OUT_OF_RANGE), like a cached index. */
+ * term NaN (KD_CHECK=1: KD_ERR_IDX_OUT_OF_RANGE), like a cached index.
+ *
+ * student = KD_STUDENT_RENORM is the other loss-design reading: the student's
+ * softmax over the row's K cached entries only, like the teacher's (a = 0 only):
+ *   lseK[i] = log sum_k exp(z[i, idx[i,k]])          (every cached entry its own atom)
+ *   KL[i]   = sum_k p[i,k] (log p[i,k] - z[i, idx[i,k]] + lseK[i]),  loss = mean over C
+ *   dZ[i,v] = (g/|C|) sum_{k: idx[i,k]=v} (exp(z[i, idx[i,k]] - lseK[i]) - p[i,k])  for i in C
+ * dZ is zero off the cached entries, so the logits are formed at the cached entries
+ * only (no vocabulary-wide product in the forward; dH gathers W rows).  lse_out
+ * receives lseK (NaN on ignored rows), and the backward takes it as `lse`.
+ * KD_ERR_BAD_OPTION: student outside kd_student, or KD_STUDENT_RENORM with a > 0. */
+typedef enum { KD_STUDENT_FULL = 0, KD_STUDENT_RENORM = 1 } kd_student;
+
 typedef struct {
   const int32_t* labels;  /* [N] int32 DEVICE array (4-byte aligned), or NULL */
   int32_t ignore_index;   /* label value of a row left out (e.g. -100 for padding) */
   float ce_weight;        /* a in [0, 1]; > 0 needs labels */
+  int32_t student;        /* kd_student: KD_STUDENT_FULL (0, the loss above) or KD_STUDENT_RENORM */
 } kd_loss_opts;
 
 /* kd_chunked_kl_fwd with loss options (NULL = kd_chunked_kl_fwd). rows_out [N]
@@ -255,7 +268,7 @@ kd_status kd_profile_begin(void);
  * or read (the launches it would have timed are left out of the entries). */
 kd_status kd_profile_end(kd_kernel_stat* out, int max, int* n);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor): 102 adds kd_loss_opts.student. */
 int kd_version(void);
 
 #ifdef __cplusplus

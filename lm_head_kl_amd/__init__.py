@@ -71,12 +71,17 @@ class KDProblem(ctypes.Structure):
     ]
 
 
+KD_STUDENT_FULL, KD_STUDENT_RENORM = 0, 1
+_STUDENT = {"full": KD_STUDENT_FULL, "renorm": KD_STUDENT_RENORM}
+
+
 class KDLossOpts(ctypes.Structure):
     """Mirror of ``kd_loss_opts``."""
     _fields_ = [
         ("labels", ctypes.c_void_p),
         ("ignore_index", ctypes.c_int32),
         ("ce_weight", ctypes.c_float),
+        ("student", ctypes.c_int32),
     ]
 
 
@@ -256,27 +261,32 @@ def kd_topk_cache_build(h_t: torch.Tensor, w_t: torch.Tensor, k: int, chunk_toke
     return idx, val
 
 
-def _opts(labels: Optional[torch.Tensor], ignore_index: int, ce_weight: float, n: int
+def _opts(labels: Optional[torch.Tensor], ignore_index: int, ce_weight: float, n: int, student: str = "full"
           ) -> Optional[KDLossOpts]:
-    """The loss options, or None for the plain loss (no labels and no mix)."""
+    """The loss options, or None for the plain loss (no labels, no mix, the
+    full-vocabulary student)."""
     if not -2**31 <= int(ignore_index) < 2**31:
         raise ValueError("ignore_index must fit in int32")
-    if labels is None and ce_weight == 0.0:
+    if student not in _STUDENT:
+        raise ValueError("student must be 'full' or 'renorm'")
+    if labels is None and ce_weight == 0.0 and student == "full":
         return None
     if labels is not None and (labels.dtype != torch.int32 or labels.shape != (n,)):
         raise ValueError("labels must be int32 [N]")
-    return KDLossOpts(_ptr(labels), int(ignore_index), float(ce_weight))
+    return KDLossOpts(_ptr(labels), int(ignore_index), float(ce_weight), _STUDENT[student])
 
 
 def kd_chunked_kl_fwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, tau: float,
                       with_rows: bool = False, chunk_tokens: int = 0, labels: Optional[torch.Tensor] = None,
-                      ignore_index: int = -100, ce_weight: float = 0.0
+                      ignore_index: int = -100, ce_weight: float = 0.0, student: str = "full"
                       ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
     """Returns ``(loss [] float32, lse [N] float32, rows [N] float32 or None)``.
 
     With ``labels`` (int32 [N]), rows labelled ``ignore_index`` are left out and
     the mean runs over the others; ``ce_weight`` a mixes in the cross-entropy
-    with the labels: row term ``(1 - a) KL + a CE`` (``rows`` holds those terms)."""
+    with the labels: row term ``(1 - a) KL + a CE`` (``rows`` holds those terms).
+    ``student="renorm"`` takes the student's softmax over the row's K cached
+    entries only (``lse`` then holds that normaliser)."""
     n, d, v, k = _loss_inputs(h, w, idx, val)
     dev = _need_gpu(h, w, idx, val, labels)
     prob = make_problem(n, d, v, k, tau, _dt(h.dtype), _dt(val.dtype), KD_F32, chunk_tokens)
@@ -284,7 +294,7 @@ def kd_chunked_kl_fwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: 
     lse = torch.empty((n,), dtype=torch.float32, device=dev)
     rows = torch.empty((n,), dtype=torch.float32, device=dev) if with_rows else None
     ws = _workspace(KD_OP_KL_FWD, prob, dev)
-    opts = _opts(labels, ignore_index, ce_weight, n)
+    opts = _opts(labels, ignore_index, ce_weight, n, student)
     lib = load_library()
     with torch.cuda.device(dev):
         if opts is None:
@@ -301,7 +311,7 @@ def kd_chunked_kl_fwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: 
 def kd_chunked_kl_fwd_noalloc(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, tau: float,
                               loss: torch.Tensor, lse: torch.Tensor, rows: Optional[torch.Tensor] = None,
                               chunk_tokens: int = 0, labels: Optional[torch.Tensor] = None,
-                              ignore_index: int = -100, ce_weight: float = 0.0) -> None:
+                              ignore_index: int = -100, ce_weight: float = 0.0, student: str = "full") -> None:
     """The forward into caller-provided outputs (``loss`` float32 scalar, ``lse``
     float32 [N], ``rows`` float32 [N] or None), with the library's fixed scratch
     array as workspace: nothing is allocated, by the library or here."""
@@ -311,7 +321,7 @@ def kd_chunked_kl_fwd_noalloc(h: torch.Tensor, w: torch.Tensor, idx: torch.Tenso
                                                                                    or rows.shape != (n,))):
         raise ValueError("loss must be a float32 scalar and rows float32 [N]")
     prob = make_problem(n, d, v, k, tau, _dt(h.dtype), _dt(val.dtype), KD_F32, chunk_tokens)
-    opts = _opts(labels, ignore_index, ce_weight, n)
+    opts = _opts(labels, ignore_index, ce_weight, n, student)
     with torch.cuda.device(dev):
         _check(load_library().kd_chunked_kl_fwd_noalloc(ctypes.byref(prob), None if opts is None else ctypes.byref(opts),
                                                          _ptr(h), _ptr(w), _ptr(idx), _ptr(val), _ptr(loss), _ptr(lse),
@@ -321,10 +331,10 @@ def kd_chunked_kl_fwd_noalloc(h: torch.Tensor, w: torch.Tensor, idx: torch.Tenso
 def kd_chunked_kl_bwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: torch.Tensor, tau: float,
                       lse: torch.Tensor, grad: Optional[torch.Tensor] = None, dh_dtype: torch.dtype = torch.float32,
                       chunk_tokens: int = 0, labels: Optional[torch.Tensor] = None, ignore_index: int = -100,
-                      ce_weight: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor]:
+                      ce_weight: float = 0.0, student: str = "full") -> Tuple[torch.Tensor, torch.Tensor]:
     """Returns ``(dH [N,d] dh_dtype, dW [V,d] float32)`` for upstream gradient
     ``grad`` (a device scalar; None means 1).  ``labels`` / ``ignore_index`` /
-    ``ce_weight`` must be those of the forward call."""
+    ``ce_weight`` / ``student`` must be those of the forward call."""
     n, d, v, k = _loss_inputs(h, w, idx, val, lse)
     dev = _need_gpu(h, w, idx, val, lse, grad, labels)
     if grad is not None and (grad.dtype != torch.float32 or grad.numel() != 1):
@@ -333,7 +343,7 @@ def kd_chunked_kl_bwd(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, val: 
     dh = torch.empty((n, d), dtype=dh_dtype, device=dev)
     dw = torch.empty((v, d), dtype=torch.float32, device=dev)
     ws = _workspace(KD_OP_KL_BWD, prob, dev)
-    opts = _opts(labels, ignore_index, ce_weight, n)
+    opts = _opts(labels, ignore_index, ce_weight, n, student)
     lib = load_library()
     with torch.cuda.device(dev):
         if opts is None:
@@ -367,14 +377,16 @@ class KDChunkedKL(torch.autograd.Function):
     ignore_index, ce_weight])``; gradients flow to H and W."""
 
     @staticmethod
-    def forward(ctx, h, w, idx, val, tau, chunk_tokens=0, labels=None, ignore_index=-100, ce_weight=0.0):
+    def forward(ctx, h, w, idx, val, tau, chunk_tokens=0, labels=None, ignore_index=-100, ce_weight=0.0,
+                student="full"):
         loss, lse, _ = kd_chunked_kl_fwd(h, w, idx, val, tau, chunk_tokens=chunk_tokens, labels=labels,
-                                         ignore_index=ignore_index, ce_weight=ce_weight)
+                                         ignore_index=ignore_index, ce_weight=ce_weight, student=student)
         ctx.save_for_backward(h, w, idx, val, lse, labels)
         ctx.tau = tau
         ctx.chunk_tokens = chunk_tokens
         ctx.ignore_index = ignore_index
         ctx.ce_weight = ce_weight
+        ctx.student = student
         return loss
 
     @staticmethod
@@ -384,17 +396,18 @@ class KDChunkedKL(torch.autograd.Function):
         dh, dw = kd_chunked_kl_bwd(h, w, idx, val, ctx.tau, lse, g,
                                    dh_dtype=torch.float32 if h.dtype == torch.float32 else torch.bfloat16,
                                    chunk_tokens=ctx.chunk_tokens, labels=labels, ignore_index=ctx.ignore_index,
-                                   ce_weight=ctx.ce_weight)
-        return dh.to(h.dtype), dw.to(w.dtype), None, None, None, None, None, None, None
+                                   ce_weight=ctx.ce_weight, student=ctx.student)
+        return dh.to(h.dtype), dw.to(w.dtype), None, None, None, None, None, None, None, None
 
 
 def chunked_kl_loss(h, w, idx, val, tau: float = 1.0, chunk_tokens: int = 0, labels=None,
-                    ignore_index: int = -100, ce_weight: float = 0.0) -> torch.Tensor:
+                    ignore_index: int = -100, ce_weight: float = 0.0, student: str = "full") -> torch.Tensor:
     """Mean top-K KL over the tokens (autograd).  ``labels`` (int32 [N]) leave out
     the rows labelled ``ignore_index``; ``ce_weight`` mixes in the cross-entropy
-    with the labels."""
+    with the labels; ``student="renorm"`` normalises the student over the cached
+    entries only."""
     return KDChunkedKL.apply(h, w, idx, val, float(tau), int(chunk_tokens), labels, int(ignore_index),
-                             float(ce_weight))
+                             float(ce_weight), student)
 
 
 class ChunkedTopKKLLoss(torch.nn.Module):
@@ -411,12 +424,15 @@ class ChunkedTopKKLLoss(torch.nn.Module):
     the labels' cross-entropy when ``ce_weight`` > 0."""
 
     def __init__(self, tau: float = 1.0, ignore_index: int = -100, ce_weight: float = 0.0,
-                 chunk_tokens: int = 0):
+                 chunk_tokens: int = 0, student: str = "full"):
         super().__init__()
         self.tau = float(tau)
         self.ignore_index = int(ignore_index)
         self.ce_weight = float(ce_weight)
         self.chunk_tokens = int(chunk_tokens)
+        if student not in _STUDENT:
+            raise ValueError("student must be 'full' or 'renorm'")
+        self.student = student
 
     def forward(self, hidden, weight, idx, val, labels=None):
         d = hidden.shape[-1]
@@ -433,11 +449,11 @@ class ChunkedTopKKLLoss(torch.nn.Module):
             wide = (lab < -2**31) | (lab >= 2**31)
             lab = torch.where(wide, torch.full_like(lab, bad), lab).to(torch.int32)
         return chunked_kl_loss(h, weight, idx.view(-1, k), val.view(-1, k), self.tau, self.chunk_tokens, lab,
-                               self.ignore_index, self.ce_weight)
+                               self.ignore_index, self.ce_weight, self.student)
 
     def extra_repr(self) -> str:
         return (f"tau={self.tau}, ignore_index={self.ignore_index}, ce_weight={self.ce_weight}, "
-                f"chunk_tokens={self.chunk_tokens}")
+                f"chunk_tokens={self.chunk_tokens}, student={self.student!r}")
 
 
 # ---- on-disk cache shards and the streaming loader (include/kdcache.h)

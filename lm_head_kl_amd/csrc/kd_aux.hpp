@@ -32,76 +32,197 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh /* >= 32 ints */, 
 
 // ---------------------------------------------------------------------------
 // Bucket the cache entries of one 256-token tile by 256-wide vocabulary tile, so
-// the forward GEMM epilogue of tile (tx, ty) reads exactly the entries that fall
-// inside it.  Entry = token (8 bits) | vocab within tile (8 bits) | k (16 bits).
+// the GEMM epilogues of tile (tx, ty) read exactly the entries that fall inside
+// it.  Entry = token (8 bits) | vocab within tile (8 bits) | k (16 bits).
 // Out-of-range indices are skipped and flagged.  With labels, a row whose label
 // equals `ignore` contributes no entry (its cache row is not read), and with
 // add_label every other row's label is one more entry, k = kc.  Rows of entries
-// are kz apart (kc, or kc + 1 with add_label).
+// are kz apart (kc, or kc + 1 with add_label).  With `pw` ([rows][kz] weights of
+// the chunk's entries), each placed entry's weight is copied beside it into `ew`.
+//
+// With `ordered`, the order inside a bucket is fixed (no dependence on timing):
+// each of the block's waves owns a contiguous run of rows; a bucket holds the
+// entries of the first wave's rows, then the second's, and so on; within a wave,
+// its cache entries in (row, k) order, then its rows' labels in row order.  So
+// entries with the same (row, vocabulary index) appear in k order, and a consumer
+// that walks a bucket in order accumulates in a fixed order.  Without it (the
+// forward's gather, which does not depend on the order) entries take their slots
+// with LDS atomics.
+//   pass 1: per-(wave, bucket) counts (LDS atomics: counts do not depend on order);
+//   scan:   bucket offsets, and within each bucket each wave's starting cursor;
+//   pass 2: each wave walks its entries in order, 64 at a time.  The lanes that hold
+//           the same bucket form a group: each lane ORs its bit into its bucket's
+//           64-bit lane mask in the wave's LDS table (an OR does not depend on order)
+//           and reads the mask back; the group's lowest lane takes the group's slots
+//           from the wave's cursor and clears the mask, and the lane's rank in the
+//           mask gives its entry's slot.  Vocabularies too large for the mask table
+//           (ordered == 2) group the lanes with one ballot per distinct bucket.
+__device__ __forceinline__ int lane_rank(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 __global__ void __launch_bounds__(1024) bucket_kernel(const int32_t* __restrict__ idx,
                                                       const int32_t* __restrict__ labels, int ignore,
                                                       int add_label, int nr, int kc, int kz, int vocab, int n_ty,
-                                                      uint32_t* __restrict__ entries, int* __restrict__ offsets,
-                                                      int* __restrict__ bad) {
-  extern __shared__ int hist[];   // n_ty + 64 ints
+                                                      int ordered, const float* __restrict__ pw,
+                                                      uint32_t* __restrict__ entries, float* __restrict__ ew,
+                                                      int* __restrict__ offsets, int* __restrict__ bad) {
+  // LDS: [nw][n_ty] counts, then cursors; 64 ints of scan scratch; with ordered == 1
+  // a [nw][n_ty] table of 64-bit lane masks (zero between rounds)
+  extern __shared__ int cnt[];
   __shared__ int lab[BX];
-  int* sh = hist + n_ty + 1;
+  const int nw = (int)(blockDim.x >> 6);
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  int* sh = cnt + nw * n_ty;
+  // volatile: the read-back must see the LDS (the other lanes' bits), not be folded
+  // into this lane's own OR; LDS address space, so the accesses stay LDS operations
+  typedef volatile __attribute__((address_space(3))) unsigned long long lds_vu64;
+  typedef __attribute__((address_space(3))) unsigned long long lds_u64;
+  const int mask_off = (nw * n_ty + 64 + 1) & ~1;         // ints; 8-byte aligned
+  lds_vu64* lmask = (lds_vu64*)(cnt + mask_off) + (size_t)wave * n_ty;
   const int tx = blockIdx.x;
   const int r0 = tx * BX;
   const int rows = min(BX, nr - r0);
-  const int total = rows * kc;
-  const int all = total + (add_label ? rows : 0);
+  const int rpw = BX / nw;                                   // rows per wave
+  const int wr0 = min(rows, wave * rpw), wr1 = min(rows, wave * rpw + rpw);
+  const int nce = (wr1 - wr0) * kc;                          // this wave's cache entries
+  const int nall = nce + (add_label ? wr1 - wr0 : 0);
   const bool masked = labels != nullptr;
   const int32_t* src = idx + (int64_t)r0 * kc;
-  for (int b = threadIdx.x; b <= n_ty; b += blockDim.x) hist[b] = 0;
+  for (int i = threadIdx.x; i < nw * n_ty; i += blockDim.x) cnt[i] = 0;
+  if (ordered == 1)
+    for (int i = threadIdx.x; i < 2 * nw * n_ty; i += blockDim.x) cnt[mask_off + i] = 0;
   if (masked)
     for (int t = threadIdx.x; t < rows; t += blockDim.x) lab[t] = labels[r0 + t];
   __syncthreads();
-  // entry e: cache entry (t, k) for e < total, else the label of row e - total;
-  // false for a row left out, else its vocabulary index in v
-  auto entry = [&](int e, int& v, int& t, int& k) -> bool {
-    if (e < total) {
-      t = e / kc;
-      k = e - t * kc;
+  // entry j of this wave: cache entry (t, k) for j < nce, else the label of row
+  // wr0 + j - nce; false for a row left out, else its vocabulary index in v
+  auto entry = [&](int j, int& v, int& t, int& k) -> bool {
+    if (j < nce) {
+      const int q = j / kc;
+      t = wr0 + q;
+      k = j - q * kc;
     } else {
-      t = e - total;
+      t = wr0 + (j - nce);
       k = kc;
     }
     if (masked && lab[t] == ignore) return false;
-    v = e < total ? src[e] : lab[t];
+    v = j < nce ? src[(int64_t)t * kc + k] : lab[t];
     return true;
   };
+  int* mine = cnt + wave * n_ty;
   int nbad = 0;
-  for (int e = threadIdx.x; e < all; e += blockDim.x) {
+  for (int j = lane; j < nall; j += 64) {
     int v, t, k;
-    if (!entry(e, v, t, k)) continue;
-    if ((unsigned)v < (unsigned)vocab) atomicAdd(&hist[v >> 8], 1);
+    if (!entry(j, v, t, k)) continue;
+    if ((unsigned)v < (unsigned)vocab) atomicAdd(&mine[v >> 8], 1);
     else ++nbad;
   }
   if (nbad) atomicAdd(bad, nbad);
   __syncthreads();
-  // exclusive scan of hist[0..n_ty) in contiguous per-thread segments
-  const int seg = (n_ty + blockDim.x - 1) / blockDim.x;
+  // bucket offsets (exclusive scan over buckets, each thread a contiguous segment),
+  // and each wave's cursor inside every bucket
+  const int seg = (n_ty + (int)blockDim.x - 1) / (int)blockDim.x;
   const int b0 = min(n_ty, (int)threadIdx.x * seg), b1 = min(n_ty, b0 + seg);
   int local = 0;
-  for (int b = b0; b < b1; ++b) local += hist[b];
+  for (int b = b0; b < b1; ++b)
+    for (int w = 0; w < nw; ++w) local += cnt[w * n_ty + b];
   int tot;
   int run = block_excl_scan(local, sh, tot);
   int* out = offsets + (int64_t)tx * (n_ty + 1);
   for (int b = b0; b < b1; ++b) {
-    const int c = hist[b];
-    hist[b] = run;
     out[b] = run;
-    run += c;
+    for (int w = 0; w < nw; ++w) {
+      const int c = cnt[w * n_ty + b];
+      cnt[w * n_ty + b] = run;
+      run += c;
+    }
   }
   if (threadIdx.x == 0) out[n_ty] = tot;
   __syncthreads();
   uint32_t* dst = entries + (int64_t)tx * BX * kz;
-  for (int e = threadIdx.x; e < all; e += blockDim.x) {
-    int v, t, k;
-    if (entry(e, v, t, k) && (unsigned)v < (unsigned)vocab) {
-      const int pos = atomicAdd(&hist[v >> 8], 1);
-      dst[pos] = uint32_t(t) | (uint32_t(v & 255) << 8) | (uint32_t(k) << 16);
+  float* dstw = ew ? ew + (int64_t)tx * BX * kz : nullptr;
+  auto put = [&](int pos, int v, int t, int k) {
+    dst[pos] = uint32_t(t) | (uint32_t(v & 255) << 8) | (uint32_t(k) << 16);
+    if (dstw) dstw[pos] = pw[(int64_t)(r0 + t) * kz + k];
+  };
+  if (!ordered) {
+    for (int j = lane; j < nall; j += 64) {
+      int v, t, k;
+      if (entry(j, v, t, k) && (unsigned)v < (unsigned)vocab) put(atomicAdd(&mine[v >> 8], 1), v, t, k);
+    }
+    return;
+  }
+  // Eight rounds at a time: their indices and weights are loaded first (independent
+  // loads in flight together), then the rounds are placed one after the other.
+  constexpr int R = 8;
+  for (int jb = 0; jb < nall; jb += 64 * R) {
+    int vr[R];
+    float wr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int v = -1, t = 0, k = 0;
+      const int j = jb + 64 * r + lane;
+      const bool ok = j < nall && entry(j, v, t, k) && (unsigned)v < (unsigned)vocab;
+      vr[r] = ok ? v : -1;
+      wr[r] = (ok && dstw) ? pw[(int64_t)(r0 + t) * kz + k] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int j = jb + 64 * r + lane;
+      const int v = vr[r];
+      const bool ok = v >= 0;
+      int t = 0, k = 0;
+      if (ok) {
+        if (j < nce) {
+          const int q = j / kc;
+          t = wr0 + q;
+          k = j - q * kc;
+        } else {
+          t = wr0 + (j - nce);
+          k = kc;
+        }
+      }
+      const uint32_t code = uint32_t(t) | (uint32_t(v & 255) << 8) | (uint32_t(k) << 16);
+      const int b = ok ? (v >> 8) : -1;
+      int slot = 0;
+      if (ordered == 1) {
+        if (ok) __hip_atomic_fetch_or((lds_u64*)&lmask[b], 1ull << lane, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WAVEFRONT);
+        const uint64_t m = ok ? (uint64_t)lmask[b] : 0ull;
+        const int leader = ok ? __builtin_ctzll(m) : 0;
+        int pos = 0;
+        if (ok && leader == lane) {        // the group's lowest lane; groups have distinct buckets
+          pos = mine[b];
+          mine[b] = pos + __builtin_popcountll(m);
+          lmask[b] = 0ull;
+        }
+        slot = __shfl(pos, leader) + lane_rank(m);
+      } else {
+        uint64_t todo = __ballot(ok);
+        int leader = 0, rank = 0, gsize = 0;
+        while (todo) {                     // one pass per distinct bucket among the 64 entries
+          const int l = __builtin_ctzll(todo);
+          const int bl = __builtin_amdgcn_readlane(b, l);
+          const uint64_t m = __ballot(b == bl);
+          if (b == bl) {
+            leader = l;
+            rank = lane_rank(m);
+            gsize = __builtin_popcountll(m);
+          }
+          todo &= ~m;
+        }
+        int pos = 0;
+        if (ok && rank == 0) {             // the group's lowest lane; groups have distinct buckets
+          pos = mine[b];
+          mine[b] = pos + gsize;
+        }
+        slot = __shfl(pos, leader) + rank;
+      }
+      if (ok) {
+        dst[slot] = code;
+        if (dstw) dstw[slot] = wr[r];
+      }
     }
   }
 }
@@ -346,33 +467,23 @@ __global__ void __launch_bounds__(256) transpose_pad_kernel(const T* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Subtract the scaled teacher probabilities at the cached entries of each row
-// from dZ (and from dZ^T when that copy exists).  RB_ROWS rows per block, RB_TPR
-// threads per row.  Entries are applied in batches of RB_TPR in k order: within a
-// batch, repeated indices are summed (in k order) by their first occurrence, and
-// a block barrier orders the batches, so every element is updated by one thread
-// at a time and repeated indices accumulate.  With labels, rows whose label
-// equals `ignore` are left alone (their dZ row is 0 already), and with alpha > 0
-// the teacher is weighted by 1 - alpha and the label is one more entry (k = kc)
-// of weight alpha.
-template <typename T, typename VT>
-__global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ idx, const VT* __restrict__ val,
-                                                      int nr, int kc, int vocab, float inv_tau,
-                                                      const float* __restrict__ grad, float inv_n,
-                                                      const int32_t* __restrict__ labels, int ignore, float alpha,
-                                                      T* __restrict__ dz, int64_t ldz, T* __restrict__ dzt,
-                                                      int64_t ldzt) {
+// Weight of every cached entry in dZ (subtracted by the dZ GEMM epilogue):
+// pw[t][k] = (g/N)(1 - alpha) p[t][k] with p the teacher softmax of the row's K
+// cached logits over tau, and with alpha > 0 pw[t][kc] = (g/N) alpha for the label.
+// RB_ROWS rows per block, RB_TPR threads per row.  Rows whose label equals `ignore`
+// are left out (they get no bucketed entry, so their weights are never read).
+template <typename VT>
+__global__ void __launch_bounds__(256) teacher_weights_kernel(const VT* __restrict__ val, int nr, int kc, int kz,
+                                                              float inv_tau, const float* __restrict__ grad,
+                                                              float inv_n, const int32_t* __restrict__ labels,
+                                                              int ignore, float alpha, float* __restrict__ pw) {
   __shared__ float sh[4 * RB_ROWS];
-  __shared__ int bidx[RB_ROWS][RB_TPR];
-  __shared__ float bpe[RB_ROWS][RB_TPR];
   const int r = threadIdx.x & (RB_ROWS - 1), q = threadIdx.x / RB_ROWS;
   const int t = blockIdx.x * RB_ROWS + r;
   const bool counted = t < nr && (labels == nullptr || labels[t] != ignore);
   const float scale = (grad ? *grad : 1.0f) * inv_n;
   const float wt = scale * (1.0f - alpha);
-  const int ke = kc + (alpha > 0.f ? 1 : 0);
   const VT* vr = val + (int64_t)t * kc;
-  const int32_t* ir = idx + (int64_t)t * kc;
   float vmax = -INFINITY;
   if (counted)
     for (int k = q; k < kc; k += RB_TPR) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
@@ -381,29 +492,212 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
   if (counted)
     for (int k = q; k < kc; k += RB_TPR) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
   const float logZ = logf(row_sum(Z, sh));
-  for (int k0 = 0; k0 < ke; k0 += RB_TPR) {
+  if (!counted) return;
+  float* out = pw + (int64_t)t * kz;
+  for (int k = q; k < kc; k += RB_TPR) out[k] = wt * expf(to_f32<VT>(vr[k]) * inv_tau - vmax - logZ);
+  if (q == 0 && kz > kc) out[kc] = scale * alpha;
+}
+
+// ---------------------------------------------------------------------------
+// The student renormalised over the row's K cached entries (loss option): the
+// logits are needed at the cached entries only, so no vocabulary-wide product runs
+// for them.
+//
+// z[t][k] = H[t] . W[idx[t][k]] for every cached entry, in float64 (one wave per
+// entry, fixed summation order), stored as float; one block of 4 waves per row,
+// wave w taking k = w, w + 4, ...  Rows whose label equals `ignore`
+// are skipped (their cache rows are not read); an index outside [0, V) gives NaN
+// and is counted in `bad`.
+template <typename T>
+__global__ void __launch_bounds__(256) gather_dot_kernel(const T* __restrict__ h, const T* __restrict__ w,
+                                                         const int32_t* __restrict__ idx, int nr, int kc, int d,
+                                                         int vocab, const int32_t* __restrict__ labels, int ignore,
+                                                         float* __restrict__ z, int* __restrict__ bad) {
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (t >= nr || (labels != nullptr && labels[t] == ignore)) return;
+  const T* hr = h + (int64_t)t * d;
+  for (int k = wave; k < kc; k += 4) {
+    const int v = idx[(int64_t)t * kc + k];
+    float out = NAN;
+    if ((unsigned)v < (unsigned)vocab) out = (float)wave_dot_f64<T>(hr, w + (int64_t)v * d, d, lane);
+    else if (lane == 0 && bad) atomicAdd(bad, 1);
+    if (lane == 0) z[(int64_t)t * kc + k] = out;
+  }
+}
+
+// Per row: lseK = log sum_k exp(z[t][k]), the teacher softmax p over val / tau, and
+// KL = sum_k p (log p - z + lseK); lse_out = lseK (NaN on an ignored row), the
+// row's KL to kl_out, and the block's sum of KL (float64, row order) for the loss.
+// RB_ROWS rows per block, RB_TPR threads per row.
+template <typename VT>
+__global__ void __launch_bounds__(256) renorm_merge_kernel(const float* __restrict__ z, const VT* __restrict__ val,
+                                                           int nr, int kc, float inv_tau,
+                                                           const int32_t* __restrict__ labels, int ignore,
+                                                           float* __restrict__ lse_out, float* __restrict__ kl_out,
+                                                           double* __restrict__ block_sums) {
+  __shared__ float sh[4 * RB_ROWS];
+  __shared__ float klrow[RB_ROWS];
+  const int r = threadIdx.x & (RB_ROWS - 1), q = threadIdx.x / RB_ROWS;
+  const int t = blockIdx.x * RB_ROWS + r;
+  const bool valid = t < nr;
+  const bool counted = valid && (labels == nullptr || labels[t] != ignore);
+  const float* zr = z + (int64_t)t * kc;
+  const VT* vr = val + (int64_t)t * kc;
+  float zm = -INFINITY, vmax = -INFINITY;
+  if (counted)
+    for (int k = q; k < kc; k += RB_TPR) {
+      zm = fmaxf(zm, zr[k]);
+      vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
+    }
+  zm = row_max(zm, sh);
+  vmax = row_max(vmax, sh);
+  float zs = 0.f, Z = 0.f;
+  if (counted)
+    for (int k = q; k < kc; k += RB_TPR) {
+      zs += expf(zr[k] - zm);
+      Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
+    }
+  const float lk = zm + logf(row_sum(zs, sh));
+  const float logZ = logf(row_sum(Z, sh));
+  float kl = 0.f;
+  if (counted)
+    for (int k = q; k < kc; k += RB_TPR) {
+      const float lp = to_f32<VT>(vr[k]) * inv_tau - vmax - logZ;
+      const float p = expf(lp);
+      const float zk = zr[k];
+      kl += (p > 0.f ? p * lp : 0.f) - p * (zk - lk);
+      if (zk != zk) kl = NAN;
+    }
+  kl = row_sum(kl, sh);
+  if (q == 0) {
+    klrow[r] = counted ? kl : 0.f;
+    if (valid) {
+      lse_out[t] = counted ? lk : NAN;
+      if (kl_out) kl_out[t] = counted ? kl : 0.f;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (int i = 0; i < RB_ROWS; ++i) s += (double)klrow[i];
+    block_sums[blockIdx.x] = s;
+  }
+}
+
+// c[t][k] = (g/N) (exp(z[t][k] - lseK[t]) - p[t][k]): the gradient of the loss at
+// each cached entry (the logit's share; repeated indices are summed by the users of
+// c).  RB_ROWS rows per block, RB_TPR threads per row; ignored rows are skipped.
+template <typename VT>
+__global__ void __launch_bounds__(256) renorm_coef_kernel(const float* __restrict__ z, const VT* __restrict__ val,
+                                                          const float* __restrict__ lse, int nr, int kc,
+                                                          float inv_tau, const float* __restrict__ grad, float inv_n,
+                                                          const int32_t* __restrict__ labels, int ignore,
+                                                          float* __restrict__ c) {
+  __shared__ float sh[4 * RB_ROWS];
+  const int r = threadIdx.x & (RB_ROWS - 1), q = threadIdx.x / RB_ROWS;
+  const int t = blockIdx.x * RB_ROWS + r;
+  const bool counted = t < nr && (labels == nullptr || labels[t] != ignore);
+  const float scale = (grad ? *grad : 1.0f) * inv_n;
+  const VT* vr = val + (int64_t)t * kc;
+  float vmax = -INFINITY;
+  if (counted)
+    for (int k = q; k < kc; k += RB_TPR) vmax = fmaxf(vmax, to_f32<VT>(vr[k]) * inv_tau);
+  vmax = row_max(vmax, sh);
+  float Z = 0.f;
+  if (counted)
+    for (int k = q; k < kc; k += RB_TPR) Z += expf(to_f32<VT>(vr[k]) * inv_tau - vmax);
+  const float logZ = logf(row_sum(Z, sh));
+  if (!counted) return;
+  const float lk = lse[t];
+  const float* zr = z + (int64_t)t * kc;
+  float* cr = c + (int64_t)t * kc;
+  for (int k = q; k < kc; k += RB_TPR)
+    cr[k] = scale * (expf(zr[k] - lk) - expf(to_f32<VT>(vr[k]) * inv_tau - vmax - logZ));
+}
+
+// dH[t] = sum_k c[t][k] W[idx[t][k]] in k order (float32), one block per row, each
+// thread 8 consecutive columns of each 2,048-column pass.  Entries with an index
+// outside [0, V) add nothing; ignored rows (and rows with no weight) are zero.
+template <typename T, typename OT>
+__global__ void __launch_bounds__(256) renorm_dh_kernel(const T* __restrict__ w, const int32_t* __restrict__ idx,
+                                                        const float* __restrict__ c, int nr, int kc, int d, int vocab,
+                                                        const int32_t* __restrict__ labels, int ignore,
+                                                        OT* __restrict__ dh) {
+  const int t = blockIdx.x;
+  if (t >= nr) return;
+  const bool counted = labels == nullptr || labels[t] != ignore;
+  const int32_t* ir = idx + (int64_t)t * kc;
+  const float* cr = c + (int64_t)t * kc;
+  for (int j0 = threadIdx.x * 8; j0 < d; j0 += 256 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (counted)
+      for (int k = 0; k < kc; ++k) {
+        const int v = ir[k];
+        if ((unsigned)v >= (unsigned)vocab) continue;
+        const float ck = cr[k];
+        const T* wr = w + (int64_t)v * d + j0;
+        if constexpr (sizeof(T) == 2) {
+          const u32x4 x = *(const u32x4*)wr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaf(ck, __uint_as_float(x[e] << 16), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(ck, __uint_as_float(x[e] & 0xffff0000u), acc[2 * e + 1]);
+          }
+        } else {
+          const f32x4 x0 = *(const f32x4*)wr, x1 = *(const f32x4*)(wr + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[e] = fmaf(ck, x0[e], acc[e]);
+            acc[4 + e] = fmaf(ck, x1[e], acc[4 + e]);
+          }
+        }
+      }
+    OT* o = dh + (int64_t)t * d + j0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = from_f32<OT>(acc[e]);
+  }
+}
+
+// dZ[t][idx[t][k]] += c[t][k] on a zeroed dZ chunk (and dZ^T when that copy
+// exists), so that the dW product runs on it.  RB_ROWS rows per block, RB_TPR
+// threads per row; entries are applied in batches of RB_TPR in k order: within a
+// batch, repeated indices are summed (in k order) by their first occurrence, and a
+// block barrier orders the batches, so every element is updated by one thread at a
+// time and repeated indices accumulate in a fixed order.
+template <typename T>
+__global__ void __launch_bounds__(256) renorm_scatter_kernel(const int32_t* __restrict__ idx,
+                                                             const float* __restrict__ c, int nr, int kc, int vocab,
+                                                             const int32_t* __restrict__ labels, int ignore,
+                                                             T* __restrict__ dz, int64_t ldz, T* __restrict__ dzt,
+                                                             int64_t ldzt) {
+  __shared__ int bidx[RB_ROWS][RB_TPR];
+  __shared__ float bc[RB_ROWS][RB_TPR];
+  const int r = threadIdx.x & (RB_ROWS - 1), q = threadIdx.x / RB_ROWS;
+  const int t = blockIdx.x * RB_ROWS + r;
+  const bool counted = t < nr && (labels == nullptr || labels[t] != ignore);
+  for (int k0 = 0; k0 < kc; k0 += RB_TPR) {
     const int k = k0 + q;
     int v = -1;
-    float pe = 0.f;
-    if (counted && k < ke) {
-      v = k < kc ? ir[k] : labels[t];
+    float ck = 0.f;
+    if (counted && k < kc) {
+      v = idx[(int64_t)t * kc + k];
       if ((unsigned)v >= (unsigned)vocab) v = -1;
-      else pe = k < kc ? wt * expf(to_f32<VT>(vr[k]) * inv_tau - vmax - logZ) : scale * alpha;
+      else ck = c[(int64_t)t * kc + k];
     }
     bidx[r][q] = v;
-    bpe[r][q] = pe;
+    bc[r][q] = ck;
     __syncthreads();
     bool first = v >= 0;
     for (int j = 0; j < q && first; ++j) first = bidx[r][j] != v;
     if (first) {
-      float sum = pe;
+      float sum = ck;
       for (int j = q + 1; j < RB_TPR; ++j)
-        if (bidx[r][j] == v) sum += bpe[r][j];
+        if (bidx[r][j] == v) sum += bc[r][j];
       T* a = dz + (int64_t)t * ldz + v;
-      *a = from_f32<T>(to_f32<T>(*a) - sum);
+      *a = from_f32<T>(to_f32<T>(*a) + sum);
       if (dzt) {
         T* b = dzt + (int64_t)v * ldzt + t;
-        *b = from_f32<T>(to_f32<T>(*b) - sum);
+        *b = from_f32<T>(to_f32<T>(*b) + sum);
       }
     }
     __syncthreads();   // this batch's updates before the next batch's reads

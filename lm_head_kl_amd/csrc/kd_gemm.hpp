@@ -82,14 +82,14 @@ template <class C> constexpr int stage_wave_floats() { return C::WX * SPITCH; }
 template <class C> constexpr int stats_off() { return C::NWAVES * stage_wave_floats<C>() * 4; }
 template <class C> constexpr int fwd_lds() { return stats_off<C>() + C::WAVES_Y * C::BX * 8; }
 template <class C, int EPI> constexpr int kernel_lds() {
-  return (EPI == 2 && fwd_lds<C>() > C::MAIN_LDS) ? fwd_lds<C>() : C::MAIN_LDS;
+  return ((EPI == 2 || EPI == 3) && fwd_lds<C>() > C::MAIN_LDS) ? fwd_lds<C>() : C::MAIN_LDS;
 }
 
 enum Epi : int {
   EPI_STORE_F32 = 0,   // P -> float out (optionally += existing)
   EPI_STORE_BF16 = 1,  // P -> bf16 out
   EPI_KL_FWD = 2,      // per-row online (max, sum exp) partials + cached-entry gather
-  EPI_KL_DZ = 3,       // dZ = (g/N) exp(z - lse) -> dZ (and, if given, dZ^T)
+  EPI_KL_DZ = 3,       // dZ = (g/N) exp(z - lse) - (cached-entry weights) -> dZ (and, if given, dZ^T)
   EPI_TOPK = 4,        // P -> float out, plus the two largest values of each row in the tile
 };
 
@@ -113,6 +113,7 @@ struct GemmArgs {
   const float* grad;              // device scalar or null (= 1)
   float inv_n;                    // 1 / N (all tokens)
   const uint32_t* entries;        // bucketed cache entries of the chunk
+  const float* ew;                // EPI_KL_DZ: weight of each bucketed entry (subtracted from dZ)
   const int* offsets;             // [n_tx][n_ty + 1]
   int kc;                         // cache entries per row (K)
   float* zg;                      // [rows][K] gathered logits
@@ -512,30 +513,103 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
       if (row < a.nx) a.partials[(int64_t)ty * a.ld_part + row] = make_float2(M, S);
     }
   } else if constexpr (EPI == EPI_KL_DZ) {
+    // dZ in 64 x 64 blocks (one wave's tokens x 64 vocabulary columns per round),
+    // staged in the wave's LDS: (1) the softmax part, (2) minus the weights of the
+    // tile's cached entries that fall in the block, (3) one rounding to T and a
+    // row-contiguous store (and for float32 inputs a token-contiguous store of dZ^T).
     const float g = a.grad ? *a.grad : 1.0f;
     const float scale = g * a.inv_n;
     T* dz = (T*)a.out;
     T* dzt = (T*)a.out2;
+    float* sw = (float*)lds + wave * stage_wave_floats<C>();
+    const int tlo = wx * WX;
+    const int* off = a.offsets + (int64_t)tx * (a.n_ty + 1) + ty;
+    const int eb = off[0], ee = off[1];
+    const uint32_t* ent = a.entries + (int64_t)tx * BXc * a.kc;
+    const float* ewt = a.ew + (int64_t)tx * BXc * a.kc;
+    float nl[FX];
+    bool rv[FX];
 #pragma unroll
     for (int i = 0; i < FX; ++i) {
       const int n = nrow0 + i * 16;
-      if (n >= a.out_rows) continue;
-      const bool rv = n < a.nx;
-      const float nl = rv ? -a.lse[n] * kLog2e : 0.f;
+      rv[i] = n < a.nx;
+      nl[i] = rv[i] ? -a.lse[n] * kLog2e : 0.f;
+    }
+    const int row0 = x0 + tlo;
 #pragma unroll
-      for (int j = 0; j < FY; ++j) {
-        const int m = mcol + j * 16;
-        if (m >= a.out_cols) continue;
-        f32x4 v;
+    for (int rnd = 0; rnd < WY / 64; ++rnd) {
+      const int vlo = wy * WY + rnd * 64;
+      const int col0 = y0 + vlo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = (rv && m + e < a.ny) ? scale * fast_exp2(fmaf(acc[i][j][e], kLog2e, nl)) : 0.f;
-        store4<T>(dz + (int64_t)n * a.ldo + m, v);
-        if (dzt) {
+      for (int i = 0; i < FX; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dzt[(int64_t)(m + e) * a.ldo2 + n] = from_f32<T>(v[e]);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int m = mcol + (rnd * 4 + jj) * 16;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = (rv[i] && m + e < a.ny) ? scale * fast_exp2(fmaf(acc[i][rnd * 4 + jj][e], kLog2e, nl[i])) : 0.f;
+          *(f32x4*)(sw + (i * 16 + (lane & 15)) * SPITCH + jj * 16 + (lane >> 4) * 4) = v;
+        }
+      wave_sync_lds();
+      // Entries of this block: lanes take 64 bucket entries at a time; lanes that hold
+      // the same (token, column) form a group whose lowest lane subtracts the group's
+      // summed weights, added in lane order (the bucket's order, which is k order for
+      // one token and column), so repeated indices accumulate in a fixed order.
+      for (int e0 = eb; e0 < ee; e0 += 64) {
+        const int e = e0 + lane;
+        int key = -1;
+        float wgt = 0.f;
+        if (e < ee) {
+          const uint32_t u = ent[e];
+          const int t = int(u & 255u) - tlo, v = int((u >> 8) & 255u) - vlo;
+          if (t >= 0 && t < WX && v >= 0 && v < 64) {
+            key = t * SPITCH + v;
+            wgt = ewt[e];
+          }
+        }
+        uint64_t todo = __ballot(key >= 0);
+        while (todo) {
+          const int l = __builtin_ctzll(todo);
+          const int kl = __builtin_amdgcn_readlane(key, l);
+          const uint64_t m = __ballot(key == kl);
+          float sum = 0.f;
+          for (uint64_t mm = m; mm; mm &= mm - 1)
+            sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), __builtin_ctzll(mm)));
+          if (lane == l) sw[kl] -= sum;
+          todo &= ~m;
         }
       }
+      wave_sync_lds();
+      if (row0 < a.out_rows && col0 < a.out_cols) {
+        if constexpr (sizeof(T) == 2) {
+          // 8 rows per store instruction, 8 lanes x 16 bytes per 64-column row segment
+#pragma unroll
+          for (int r8 = 0; r8 < 64; r8 += 8) {
+            const int r = r8 + (lane >> 3), c = (lane & 7) * 8;
+            const float* q = sw + r * SPITCH + c;
+            const f32x4 lo = *(const f32x4*)q, hi = *(const f32x4*)(q + 4);
+            u32x4 w;
+            w[0] = uint32_t(f32_to_bf16(lo[0])) | (uint32_t(f32_to_bf16(lo[1])) << 16);
+            w[1] = uint32_t(f32_to_bf16(lo[2])) | (uint32_t(f32_to_bf16(lo[3])) << 16);
+            w[2] = uint32_t(f32_to_bf16(hi[0])) | (uint32_t(f32_to_bf16(hi[1])) << 16);
+            w[3] = uint32_t(f32_to_bf16(hi[2])) | (uint32_t(f32_to_bf16(hi[3])) << 16);
+            if (row0 + r < a.out_rows) *(u32x4*)(dz + (int64_t)(row0 + r) * a.ldo + col0 + c) = w;
+          }
+        } else {
+          // 4 rows per store instruction, 16 lanes x 16 bytes per row segment
+#pragma unroll
+          for (int r4 = 0; r4 < 64; r4 += 4) {
+            const int r = r4 + (lane >> 4), c = (lane & 15) * 4;
+            if (row0 + r < a.out_rows) *(f32x4*)(dz + (int64_t)(row0 + r) * a.ldo + col0 + c) = *(const f32x4*)(sw + r * SPITCH + c);
+          }
+          if (dzt && row0 + lane < a.out_rows) {
+            // dZ^T: lane = token, so each store covers 64 consecutive tokens of one column
+            for (int c = 0; c < 64; ++c) dzt[(int64_t)(col0 + c) * a.ldo2 + row0 + lane] = sw[lane * SPITCH + c];
+          }
+        }
+      }
+      wave_sync_lds();
     }
   }
 }

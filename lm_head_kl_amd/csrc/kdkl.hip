@@ -68,7 +68,7 @@ struct Plan {
 // Workspace regions, each 256-byte aligned, in bytes from the workspace start.
 struct Layout {
   size_t entries, offsets, zg, partials, block_sums, flags;       // forward
-  size_t wt, ht, dz, dzt, dhp, lse_eff;                           // backward
+  size_t wt, ht, dz, dzt, dhp, lse_eff, pw, ew;                   // backward
   size_t count;                                                   // counted rows (+ gradient scale)
   size_t s, bmax, wmax, overflow, tops, todo;                     // cache build
   size_t total;
@@ -171,6 +171,12 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     if (part) L->dhp = take((size_t)(4 * part));
     L->lse_eff = take(sizeof(float) * (size_t)pl.Nc);
     L->count = take(16);
+    // the chunk's cached entries (and labels) bucketed per tile, with their weights
+    L->entries = take(sizeof(uint32_t) * pl.Nc * (pl.K + 1));
+    L->offsets = take(sizeof(int) * n_tx * (pl.n_ty + 1));
+    L->pw = take(sizeof(float) * pl.Nc * (pl.K + 1));
+    L->ew = take(sizeof(float) * pl.Nc * (pl.K + 1));
+    L->flags = take(sizeof(int) * 4);
   } else {
     L->s = take(sizeof(float) * (size_t)(pl.Nc * pl.ld_v));
     L->bmax = take(sizeof(double) * 1024);
@@ -323,6 +329,7 @@ struct Opts {
   const int32_t* labels = nullptr;
   int ignore = 0;
   float alpha = 0.f;
+  bool renorm = false;   // student softmax over the row's K cached entries only
 };
 
 // Counted rows (double) and, with `scale`, g / count (float) into ws + L.count.
@@ -335,10 +342,83 @@ kd_status count_rows(const Plan& pl, const Layout& L, const Opts& o, const float
   });
 }
 
+// Bucketed cache entries of one chunk (bucket_kernel): one block per 256-token tile,
+// as many waves (up to 16) as leave the per-wave tables of all waves in 64 KB of LDS
+// with the kernel's 1 KB of labels and 256 bytes of scan scratch: counters, and with
+// `ordered` (the backward's weighted entries, whose order inside each bucket is
+// fixed) 64-bit lane masks; fewer waves mean more rows per wave.  A vocabulary too
+// large for the mask table at one wave orders its buckets with ballots instead.
+kd_status run_bucket(const Plan& pl, const int32_t* idx_c, const int32_t* lab_c, const Opts& o, int add_label, int nr,
+                     int kz, bool ordered, const float* pw, uint32_t* entries, float* ew, int* offsets, int* flags,
+                     hipStream_t st) {
+  const int64_t budget = 16384 - 64 - 1 - BX;   // ints (64 of scan scratch, 1 of mask alignment)
+  int mode = ordered ? 1 : 0;
+  if (mode == 1 && 3 * (int64_t)pl.n_ty > budget) mode = 2;
+  const int tables = mode == 1 ? 3 : 1;
+  int nw = 16;
+  while (nw > 1 && (int64_t)tables * nw * pl.n_ty > budget) nw >>= 1;
+  const size_t lds = sizeof(int) * ((size_t)tables * nw * pl.n_ty + 64 + 1);
+  const int n_tx = (int)cdiv(nr, BX);
+  return launch(ordered ? "bucket_ordered" : "bucket", 0.0, 12.0 * nr * kz, st, [&] {
+    hipLaunchKernelGGL(bucket_kernel, dim3(n_tx), dim3(64 * nw), lds, st, idx_c, lab_c, o.ignore, add_label, nr,
+                       pl.K, kz, (int)pl.V, pl.n_ty, mode, pw, entries, ew, offsets, flags);
+  });
+}
+
+// Forward with the student renormalised over the cached entries: the logits at the
+// cached entries (gather_dot), then per row the normaliser over them, the teacher
+// softmax and the KL; the loss as in the full forward.
+template <typename T>
+kd_status fwd_renorm_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
+                          const void* val, float* loss, float* lse, float* kl_rows, char* ws, hipStream_t st,
+                          const Opts& o) {
+  float* zg = (float*)(ws + L.zg);
+  double* bsums = (double*)(ws + L.block_sums);
+  int* flags = (int*)(ws + L.flags);
+  const bool check = debug_checks();
+  if (check) KD_TRY(zero_words(flags, 4, st));
+  const float inv_tau = 1.0f / pl.tau;
+  const int64_t es = (int64_t)sizeof(T);
+  if (o.labels) KD_TRY(count_rows(pl, L, o, nullptr, false, ws, st));
+  for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
+    const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
+    const int32_t* idx_c = idx + r0 * pl.K;
+    const int32_t* lab_c = o.labels ? o.labels + r0 : nullptr;
+    KD_TRY(launch("gather_dot", 2.0 * nr * pl.K * (double)pl.d, (double)nr * pl.K * (es * pl.d + 8.0), st, [&] {
+      hipLaunchKernelGGL(gather_dot_kernel<T>, dim3(nr), dim3(256), 0, st, (const T*)h + r0 * pl.d, (const T*)w,
+                         idx_c, nr, pl.K, (int)pl.d, (int)pl.V, lab_c, o.ignore, zg, flags);
+    }));
+    const int nb = (int)cdiv(nr, RB_ROWS);
+    KD_TRY(launch("renorm_merge", 0.0, (double)nr * pl.K * (4.0 + (pl.vdt == KD_BF16 ? 2 : 4)), st, [&] {
+      if (pl.vdt == KD_BF16)
+        hipLaunchKernelGGL(renorm_merge_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, zg,
+                           (const bf16_t*)val + r0 * pl.K, nr, pl.K, inv_tau, lab_c, o.ignore, lse + r0,
+                           kl_rows ? kl_rows + r0 : nullptr, bsums + r0 / RB_ROWS);
+      else
+        hipLaunchKernelGGL(renorm_merge_kernel<float>, dim3(nb), dim3(256), 0, st, zg, (const float*)val + r0 * pl.K,
+                           nr, pl.K, inv_tau, lab_c, o.ignore, lse + r0, kl_rows ? kl_rows + r0 : nullptr,
+                           bsums + r0 / RB_ROWS);
+    }));
+  }
+  const int nb_all = (int)cdiv(pl.N, RB_ROWS);
+  KD_TRY(launch("loss", 0.0, 8.0 * nb_all, st, [&] {
+    hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsums, nb_all, pl.N > 0 ? 1.0 / (double)pl.N : 0.0,
+                       o.labels ? (const double*)(ws + L.count) : nullptr, loss);
+  }));
+  if (check) {
+    int bad = 0;
+    if (hipMemcpyAsync(&bad, flags, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return KD_ERR_LAUNCH;
+    if (hipStreamSynchronize(st) != hipSuccess) return KD_ERR_LAUNCH;
+    if (bad) return KD_ERR_IDX_OUT_OF_RANGE;
+  }
+  return KD_OK;
+}
+
 template <typename T>
 kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
                    const void* val, float* loss, float* lse, float* kl_rows, char* ws, hipStream_t st,
                    const Opts& o) {
+  if (o.renorm) return fwd_renorm_impl<T>(pl, L, h, w, idx, val, loss, lse, kl_rows, ws, st, o);
   uint32_t* entries = (uint32_t*)(ws + L.entries);
   int* offsets = (int*)(ws + L.offsets);
   float* zg = (float*)(ws + L.zg);
@@ -354,14 +434,9 @@ kd_status fwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
   if (o.labels) KD_TRY(count_rows(pl, L, o, nullptr, false, ws, st));
   for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
     const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
-    const int n_tx = (int)cdiv(nr, BX);
     const int32_t* idx_c = idx + r0 * pl.K;
     const int32_t* lab_c = o.labels ? o.labels + r0 : nullptr;
-    const size_t hist_bytes = sizeof(int) * (pl.n_ty + 64);
-    KD_TRY(launch("bucket", 0.0, 12.0 * nr * kz, st, [&] {
-      hipLaunchKernelGGL(bucket_kernel, dim3(n_tx), dim3(1024), hist_bytes, st, idx_c, lab_c, o.ignore, add_label,
-                         nr, pl.K, kz, (int)pl.V, pl.n_ty, entries, offsets, flags);
-    }));
+    KD_TRY(run_bucket(pl, idx_c, lab_c, o, add_label, nr, kz, false, nullptr, entries, nullptr, offsets, flags, st));
     GemmArgs g = gemm_args((const T*)h + r0 * pl.d, pl.d, nr, w, pl.d, (int)pl.V, (int)pl.d);
     g.entries = entries;
     g.offsets = offsets;
@@ -405,11 +480,86 @@ kd_status run_dh(const GemmArgs& g, bool w_kmajor, int64_t out_bytes, hipStream_
   return run_gemm<T, EPI>("gemm_dh", g, out_bytes, st);
 }
 
+// Backward with the student renormalised over the cached entries.  dZ is zero off
+// each row's cached entries: per chunk the logits at the entries again (gather_dot),
+// their gradient c = (g/N)(q - p), dH by a gather of W rows weighted by c, and dW by
+// the dW product on a dZ chunk that holds c at the cached entries and zeros
+// elsewhere (the same product, and summation order, as the full backward).
+template <typename T>
+kd_status bwd_renorm_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
+                          const void* val, const float* lse, const float* grad, void* dh, float* dw, char* ws,
+                          hipStream_t st, const Opts& o) {
+  constexpr bool kKm = std::is_same<T, bf16_t>::value;
+  T* ht = (T*)(ws + L.ht);
+  T* dz = (T*)(ws + L.dz);
+  T* dzt = kKm ? nullptr : (T*)(ws + L.dzt);
+  float* zg = (float*)(ws + L.ew);
+  float* cf = (float*)(ws + L.pw);
+  float inv_n = 1.0f / (float)pl.N;
+  const float inv_tau = 1.0f / pl.tau;
+  const int64_t es = (int64_t)sizeof(T);
+  if (o.labels) {
+    KD_TRY(count_rows(pl, L, o, grad, true, ws, st));
+    grad = (const float*)(ws + L.count + 8);
+    inv_n = 1.0f;
+  }
+  for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
+    const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
+    const int nr64 = (int)round_up(nr, 64);
+    const T* hc = (const T*)h + r0 * pl.d;
+    const int32_t* idx_c = idx + r0 * pl.K;
+    const int32_t* lab_c = o.labels ? o.labels + r0 : nullptr;
+    const int nb = (int)cdiv(nr, RB_ROWS);
+    KD_TRY(launch("gather_dot", 2.0 * nr * pl.K * (double)pl.d, (double)nr * pl.K * (es * pl.d + 8.0), st, [&] {
+      hipLaunchKernelGGL(gather_dot_kernel<T>, dim3(nr), dim3(256), 0, st, hc, (const T*)w, idx_c, nr, pl.K,
+                         (int)pl.d, (int)pl.V, lab_c, o.ignore, zg, (int*)nullptr);
+    }));
+    KD_TRY(launch("renorm_coef", 0.0, (double)nr * pl.K * (8.0 + (pl.vdt == KD_BF16 ? 2 : 4)), st, [&] {
+      if (pl.vdt == KD_BF16)
+        hipLaunchKernelGGL(renorm_coef_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, zg, (const bf16_t*)val + r0 * pl.K,
+                           lse + r0, nr, pl.K, inv_tau, grad, inv_n, lab_c, o.ignore, cf);
+      else
+        hipLaunchKernelGGL(renorm_coef_kernel<float>, dim3(nb), dim3(256), 0, st, zg, (const float*)val + r0 * pl.K,
+                           lse + r0, nr, pl.K, inv_tau, grad, inv_n, lab_c, o.ignore, cf);
+    }));
+    KD_TRY(launch("renorm_dh", 2.0 * nr * pl.K * (double)pl.d, (double)nr * pl.K * es * pl.d, st, [&] {
+      if (pl.dhdt == KD_F32)
+        hipLaunchKernelGGL((renorm_dh_kernel<T, float>), dim3(nr), dim3(256), 0, st, (const T*)w, idx_c, cf, nr,
+                           pl.K, (int)pl.d, (int)pl.V, lab_c, o.ignore, (float*)dh + r0 * pl.d);
+      else
+        hipLaunchKernelGGL((renorm_dh_kernel<T, bf16_t>), dim3(nr), dim3(256), 0, st, (const T*)w, idx_c, cf, nr,
+                           pl.K, (int)pl.d, (int)pl.V, lab_c, o.ignore, (bf16_t*)dh + r0 * pl.d);
+    }));
+    // dZ chunk: zeros, then c at the cached entries
+    KD_TRY(zero_words(dz, es * nr64 * pl.ld_v / 4, st));
+    if (dzt) KD_TRY(zero_words(dzt, es * pl.V_pad * pl.ld_t / 4, st));
+    KD_TRY(launch("renorm_scatter", 0.0, (double)nr * pl.K * (8.0 + 2.0 * es), st, [&] {
+      hipLaunchKernelGGL(renorm_scatter_kernel<T>, dim3(nb), dim3(256), 0, st, idx_c, cf, nr, pl.K, (int)pl.V, lab_c,
+                         o.ignore, dz, pl.ld_v, dzt, pl.ld_t);
+    }));
+    KD_TRY(launch("transpose_h", 0.0, 2.0 * es * nr * pl.d, st, [&] {
+      hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(nr64, 64), (unsigned)cdiv(pl.d, 64)),
+                         dim3(256), 0, st, hc, pl.d, nr, (int)pl.d, ht, pl.ld_t, nr64);
+    }));
+    GemmArgs gw = kKm ? gemm_args(dz, pl.ld_v, (int)pl.V, ht, pl.ld_t, (int)pl.d, nr64)
+                      : gemm_args(dzt, pl.ld_t, (int)pl.V, ht, pl.ld_t, (int)pl.d, nr64);
+    gw.krows_x = nr;
+    gw.out = dw;
+    gw.ldo = pl.d;
+    gw.out_rows = (int)pl.V;
+    gw.out_cols = (int)pl.d;
+    gw.accumulate = r0 > 0;
+    KD_TRY((run_gemm<T, EPI_STORE_F32, kKm, 0>("gemm_dw", gw, (r0 > 0 ? 8 : 4) * pl.V * pl.d, st)));
+  }
+  return KD_OK;
+}
+
 template <typename T>
 kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
                    const void* val, const float* lse, const float* grad, void* dh, float* dw, char* ws,
                    hipStream_t st, const Opts& o) {
   if (pl.N == 0) return zero_words(dw, pl.V * pl.d, st);
+  if (o.renorm) return bwd_renorm_impl<T>(pl, L, h, w, idx, val, lse, grad, dh, dw, ws, st, o);
   // W^T and H^T are cheap copies (W once, H per chunk).  dZ^T would cost a second
   // N x V write per chunk: bf16 reads dZ K-major in the dW product instead
   // (transposing LDS reads); float32 writes dZ^T from the dZ epilogue.
@@ -422,6 +572,13 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
   const float inv_tau = 1.0f / pl.tau;
   const int64_t es = (int64_t)sizeof(T);
   float* lse_eff = (float*)(ws + L.lse_eff);
+  uint32_t* entries = (uint32_t*)(ws + L.entries);
+  int* offsets = (int*)(ws + L.offsets);
+  float* pw = (float*)(ws + L.pw);
+  float* ew = (float*)(ws + L.ew);
+  int* flags = (int*)(ws + L.flags);
+  const int add_label = o.alpha > 0.f ? 1 : 0;
+  const int kz = pl.K + add_label;   // weighted entries per row: the K cached ones, then the label
   if (o.labels) {
     // the scale g / (counted rows) is computed on the device and read in place of g
     KD_TRY(count_rows(pl, L, o, grad, true, ws, st));
@@ -463,19 +620,25 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
       }));
       g.lse = lse_eff;
     }
-    KD_TRY((run_gemm<T, EPI_KL_DZ>("gemm_dz", g, (kKm ? 1 : 2) * es * nr * pl.V, st)));
-    // subtract the teacher at the cached entries
+    // the teacher's weight at every cached entry (and the label's), bucketed per
+    // tile in a fixed order; the dZ epilogue subtracts them before its one rounding
+    const int32_t* lab_c = o.labels ? o.labels + r0 : nullptr;
     const int nb = (int)cdiv(nr, RB_ROWS);
-    KD_TRY(launch("scatter", 0.0, (double)nr * pl.K * (8.0 + (kKm ? 2.0 : 4.0) * es), st, [&] {
+    KD_TRY(launch("teacher_weights", 0.0, (double)nr * (pl.K * (double)(pl.vdt == KD_BF16 ? 2 : 4) + 4.0 * kz), st,
+                  [&] {
       if (pl.vdt == KD_BF16)
-        hipLaunchKernelGGL((scatter_kernel<T, bf16_t>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
-                           (const bf16_t*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n,
-                           o.labels ? o.labels + r0 : nullptr, o.ignore, o.alpha, dz, pl.ld_v, dzt, pl.ld_t);
+        hipLaunchKernelGGL(teacher_weights_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, (const bf16_t*)val + r0 * pl.K,
+                           nr, pl.K, kz, inv_tau, grad, inv_n, lab_c, o.ignore, o.alpha, pw);
       else
-        hipLaunchKernelGGL((scatter_kernel<T, float>), dim3(nb), dim3(256), 0, st, idx + r0 * pl.K,
-                           (const float*)val + r0 * pl.K, nr, pl.K, (int)pl.V, inv_tau, grad, inv_n,
-                           o.labels ? o.labels + r0 : nullptr, o.ignore, o.alpha, dz, pl.ld_v, dzt, pl.ld_t);
+        hipLaunchKernelGGL(teacher_weights_kernel<float>, dim3(nb), dim3(256), 0, st, (const float*)val + r0 * pl.K,
+                           nr, pl.K, kz, inv_tau, grad, inv_n, lab_c, o.ignore, o.alpha, pw);
     }));
+    KD_TRY(run_bucket(pl, idx + r0 * pl.K, lab_c, o, add_label, nr, kz, true, pw, entries, ew, offsets, flags, st));
+    g.entries = entries;
+    g.offsets = offsets;
+    g.ew = ew;
+    g.kc = kz;
+    KD_TRY((run_gemm<T, EPI_KL_DZ>("gemm_dz", g, (kKm ? 1 : 2) * es * nr * pl.V, st)));
     // dH = dZ W  (P[t][j] = sum_v dZ[t][v] W^T[j][v], or W read K-major)
     GemmArgs gh = w_km ? gemm_args(dz, pl.ld_v, nr, w, pl.d, (int)pl.d, (int)pl.V_pad)
                        : gemm_args(dz, pl.ld_v, nr, wt, pl.ld_v, (int)pl.d, (int)pl.V_pad);
@@ -619,6 +782,10 @@ kd_status read_opts(const kd_problem* p, const kd_loss_opts* opts, Opts* o) {
   if (!opts) return KD_OK;
   if (!(std::isfinite(opts->ce_weight) && opts->ce_weight >= 0.f && opts->ce_weight <= 1.f))
     return KD_ERR_BAD_OPTION;
+  if (opts->student != KD_STUDENT_FULL && opts->student != KD_STUDENT_RENORM) return KD_ERR_BAD_OPTION;
+  // the cross-entropy needs the full-vocabulary normaliser
+  if (opts->student == KD_STUDENT_RENORM && opts->ce_weight > 0.f) return KD_ERR_BAD_OPTION;
+  o->renorm = opts->student == KD_STUDENT_RENORM;
   if (!opts->labels) return opts->ce_weight > 0.f ? KD_ERR_BAD_OPTION : KD_OK;
   if ((reinterpret_cast<uintptr_t>(opts->labels) & 3u) != 0) return KD_ERR_MISALIGNED;
   if (p && p->n_tokens > 0) {
@@ -785,7 +952,7 @@ const char* kd_status_string(kd_status s_in) {
   return "unknown status";
 }
 
-int kd_version(void) { return 101; }
+int kd_version(void) { return 102; }
 
 kd_status kd_profile_begin(void) {
   Prof& p = prof();

@@ -158,7 +158,7 @@ int main(int argc, char** argv) {
   void* dlab;
   HIP_OK(hipMalloc(&dlab, 4 * (size_t)N + 16));
   HIP_OK(hipMemcpy(dlab, lab, 4 * (size_t)N, hipMemcpyHostToDevice));
-  const kd_loss_opts opts = {(const int32_t*)dlab, -100, 0.25f};
+  const kd_loss_opts opts = {(const int32_t*)dlab, -100, 0.25f, KD_STUDENT_FULL};
   KD_OK_OR_FAIL(kd_chunked_kl_fwd_ex(&p, &opts, dh_in, dw_in, (const int32_t*)didx, dval, (float*)dloss2,
                                      (float*)dlse, NULL, dws, ws_bytes, st));
   KD_OK_OR_FAIL(kd_chunked_kl_bwd_ex(&p, &opts, dh_in, dw_in, (const int32_t*)didx, dval, (const float*)dlse, NULL,

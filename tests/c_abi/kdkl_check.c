@@ -170,7 +170,7 @@ static void call_errors(void) {
   CHECK(kd_chunked_kl_fwd(&bad, h, w, idx, val, loss, lse, rows, ws, need, NULL) == KD_ERR_BAD_TAU, "fwd tau");
 
   /* loss options */
-  kd_loss_opts o = {(const int32_t*)buf[6], -100, 0.5f};
+  kd_loss_opts o = {(const int32_t*)buf[6], -100, 0.5f, KD_STUDENT_FULL};
   const float bad_weights[] = {-0.01f, 1.01f, NAN, INFINITY};
   for (size_t i = 0; i < sizeof bad_weights / sizeof bad_weights[0]; ++i) {
     o.ce_weight = bad_weights[i];
@@ -199,6 +199,27 @@ static void call_errors(void) {
   CHECK(kd_chunked_kl_fwd_ex(&p, NULL, h, w, idx, val, loss, lse, rows, ws, small, NULL) ==
             KD_ERR_WORKSPACE_TOO_SMALL,
         "fwd_ex NULL options");
+  /* the student normaliser: only the two kd_student values, and no mix with the renormalised one */
+  const int32_t bad_students[] = {-1, 2, 1000};
+  for (size_t i = 0; i < sizeof bad_students / sizeof bad_students[0]; ++i) {
+    o.student = bad_students[i];
+    CHECK(kd_chunked_kl_fwd_ex(&p, &o, h, w, idx, val, loss, lse, rows, ws, need, NULL) == KD_ERR_BAD_OPTION,
+          "fwd_ex student %d", (int)bad_students[i]);
+    CHECK(kd_chunked_kl_bwd_ex(&p, &o, h, w, idx, val, lse, NULL, buf[3], (float*)buf[4], ws, small, NULL) ==
+              KD_ERR_BAD_OPTION,
+          "bwd_ex student %d", (int)bad_students[i]);
+  }
+  o.student = KD_STUDENT_RENORM;
+  o.labels = (const int32_t*)buf[6];
+  o.ce_weight = 0.25f;
+  CHECK(kd_chunked_kl_fwd_ex(&p, &o, h, w, idx, val, loss, lse, rows, ws, need, NULL) == KD_ERR_BAD_OPTION,
+        "fwd_ex renormalised student with a mix");
+  o.ce_weight = 0.f;
+  CHECK(kd_chunked_kl_fwd_ex(&p, &o, h, w, idx, val, loss, lse, rows, ws, small, NULL) ==
+            KD_ERR_WORKSPACE_TOO_SMALL,
+        "fwd_ex renormalised student");
+  o.student = KD_STUDENT_FULL;
+  o.labels = NULL;
 
   /* backward */
   size_t need_b = 0;

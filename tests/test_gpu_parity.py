@@ -231,18 +231,22 @@ def test_out_of_range_index_gives_nan_row_not_a_fault():
     assert np.isnan(loss.item())
 
 
-@pytest.mark.parametrize("k,span", [(6, None), (40, 20)])
-def test_repeated_indices_scatter_add(k, span):
+@pytest.mark.parametrize("k,span,n,d,v", [(6, None, 260, 64, 300), (40, 20, 260, 64, 300),
+                                           (40, "half", 64, 8, 1400000)])
+def test_repeated_indices_scatter_add(k, span, n, d, v):
     """Repeated indices in a row are separate entries: the gradient scatter-adds them.
-    (40, 20): every row draws 40 entries from 20 vocabulary ids, so repeats fall both
-    inside one batch of the scatter and across batches; the result is also checked
-    to be bitwise reproducible."""
-    n, d, v = 260, 64, 300
+    (40, 20): every row draws 40 entries from 20 vocabulary ids, so repeats fall in
+    one bucket of the backward's entries, inside and across its 64-entry rounds.
+    (40, "half") at V = 1,400,000: every row repeats its first 20 indices, over a
+    vocabulary whose bucket table takes the ballot grouping.  The results are also
+    checked to be bitwise reproducible."""
     p = kd_synth.small_problem(n, d, v, seed=8)
     H = kd_synth.to_float64(p["H"], "bf16")
     W = kd_synth.to_float64(p["W"], "bf16")
     idx, valb = kd_synth.random_cache(n, v, k, seed=2, distinct=False)
-    if span is not None:
+    if span == "half":
+        idx[:, k // 2:] = idx[:, :k // 2]
+    elif span is not None:
         idx = (idx % span).astype(np.int32)
     val = kd_synth.to_float64(valb, "bf16")
     ref_dH, ref_dW = oracle.kl_backward(H, W, idx, val, 1.0)

@@ -1,14 +1,29 @@
-"""Parity at the workloads' full sizes, in the launch configuration the benchmark
-uses (library-default chunking).
+"""Parity at the workloads' full sizes, with the step run exactly as the benchmark
+runs it: ``kd_chunked_kl_fwd`` with the library's default chunk and no per-row
+output, then ``kd_chunked_kl_bwd`` with bf16 dH (the bf16-store epilogue of the dH
+product, unsplit at 16K-token chunks) and the default chunk.
 
-The float64 oracle cannot evaluate every row at these sizes, so each workload is
-checked on a seeded sample of rows (always including the first and last row and
-rows on both sides of a chunk boundary) that the oracle computes one by one:
-top-K indices and values bit-exact, per-row log-sum-exp and KL, and dH rows.  dW
-needs every row; it is checked element-wise at the 4K-token workload and through
-properties that hold at any size elsewhere (every row of dZ sums to zero, so the
-columns of dW sum to zero; the loss is the mean of the per-row KL).
+What is compared, per workload:
+
+* the teacher cache of every row, bit for bit: SHA-256 digests of each 4,096-row
+  block of the GPU's idx and val against those of the oracle's cache, stored in
+  ``tests/golden/fullsize/`` by ``tests/golden/make_fullsize_golden.py`` (oracle and
+  input generator only);
+* every row's lse and KL and the loss against the oracle's, stored by the same
+  script (KL rows from a second forward call with the per-row output, whose loss
+  must equal the benchmark call's bit for bit);
+* dH and dW: at 4,096 and 32,768 tokens (both 32K workloads) and at 16,384 tokens
+  of the sweep, every element against the oracle's backward, run here on the GPU
+  host (one to two minutes each).  At 65,536 and more tokens the oracle's
+  backward over every row would take several minutes, so dH is compared on seeded
+  sample rows, and dW through properties that hold at any size: each dZ row sums
+  to zero, so dW's columns do; dW over all tokens equals the token-weighted sum of
+  dW over each chunk alone.
 """
+import hashlib
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +36,14 @@ from gpu_util import GRAD_TOL, LOSS_RTOL, LSE_RTOL, bf16_bits_of, device, rel_ma
 pytestmark = pytest.mark.gpu
 
 CHUNK = 16384   # the library's default tokens per chunk
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fullsize")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, f"{name}.json")) as f:
+        meta = json.load(f)
+    arrays = dict(np.load(os.path.join(GOLDEN, f"{name}.npz")))
+    return meta, arrays
 
 
 def sample_rows(n, count, seed):
@@ -30,47 +53,91 @@ def sample_rows(n, count, seed):
     return np.unique(np.array(fixed + list(rest), dtype=np.int64))
 
 
-def run_workload(name, n, k, rows_count=24, full_dw=False):
+def check_cache(idx, val, meta, k, n):
+    """Every row of the GPU cache against the oracle's block digests."""
+    rows = meta["digest_rows"]
+    assert n % rows == 0
+    want = meta["cache"][str(k)]
+    ih = idx.cpu().numpy()
+    vh = bf16_bits_of(val) if meta["val_dtype"] == "bf16" else val.cpu().numpy().view(np.uint32)
+    bad = []
+    for b in range(n // rows):
+        r0, r1 = b * rows, (b + 1) * rows
+        di = hashlib.sha256(np.ascontiguousarray(ih[r0:r1], dtype="<i4").tobytes()).hexdigest()
+        dv = hashlib.sha256(np.ascontiguousarray(vh[r0:r1], dtype=vh.dtype.newbyteorder("<")).tobytes()).hexdigest()
+        if di != want["idx"][b] or dv != want["val"][b]:
+            bad.append((b, di != want["idx"][b], dv != want["val"][b]))
+    assert not bad, f"cache blocks (block, idx differs, val differs) of {rows} rows: {bad[:10]}"
+
+
+def chunked_rel_err(got: torch.Tensor, ref: np.ndarray, rows: int = 8192) -> float:
+    """max |got - ref| / max |ref| without a second full-size float64 copy on the host."""
+    scale = float(np.abs(ref).max())
+    err = 0.0
+    for r0 in range(0, ref.shape[0], rows):
+        g = got[r0:r0 + rows].double().cpu().numpy()
+        err = max(err, float(np.abs(g - ref[r0:r0 + rows]).max()))
+    return err / (scale if scale > 0 else 1.0)
+
+
+def bench_step(h, wd, idx, val, tau, dh_dtype):
+    """The benchmark's step (bench.py: measure.step)."""
+    loss, lse, rows = kd.kd_chunked_kl_fwd(h, wd, idx, val, tau, chunk_tokens=0)
+    assert rows is None
+    dh, dw = kd.kd_chunked_kl_bwd(h, wd, idx, val, tau, lse, None, dh_dtype=dh_dtype, chunk_tokens=0)
+    return loss, lse, dh, dw
+
+
+def run_workload(name, n, k, full_oracle, sample=64, golden_name=None):
     w = kd_synth.WORKLOADS[name]
+    meta, arrays = golden(golden_name or name)
+    assert (meta["workload"], meta["d"], meta["vocab"], meta["tau"]) == (w.name, w.d, w.vocab, w.tau)
     print(f"[fullsize] {name} N={n} K={k}", flush=True)
     H = kd_synth.hidden(w, n)
     W = kd_synth.student_head(w)
-    WT = kd_synth.teacher_head(w)
-    h, wd, wt = to_dev(H, w.dtype), to_dev(W, w.dtype), to_dev(WT, w.dtype)
+    h, wd, wt = to_dev(H, w.dtype), to_dev(W, w.dtype), to_dev(kd_synth.teacher_head(w), w.dtype)
     idx, val = kd.kd_topk_cache_build(h, wt, k)
     del wt
-    loss, lse, rows = kd.kd_chunked_kl_fwd(h, wd, idx, val, w.tau, with_rows=True)
-    dh, dw = kd.kd_chunked_kl_bwd(h, wd, idx, val, w.tau, lse, None,
-                                  dh_dtype=torch.float32)
+    dh_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    loss, lse, dh, dw = bench_step(h, wd, idx, val, w.tau, dh_dtype)
+    loss2, lse2, rows = kd.kd_chunked_kl_fwd(h, wd, idx, val, w.tau, with_rows=True)
     torch.cuda.synchronize()
 
-    rs = sample_rows(n, rows_count, seed=n + k)
+    # the cache, every row
+    check_cache(idx, val, meta, k, n)
+    print(f"[fullsize]   cache: {n // meta['digest_rows']} blocks equal the oracle's", flush=True)
+    # loss, lse and KL, every row
+    fw = meta["forward"].get(f"{k}_{n}")
+    kl_key = next((key for key in arrays if key.startswith(f"kl_k{k}_n") and int(key.split("_n")[1]) >= n), None)
+    assert kl_key is not None, f"no stored KL rows for K={k} covering {n} rows"
+    ref_kl = arrays[kl_key][:n].astype(np.float64)
+    ref_loss = fw["loss"] if fw is not None else float(ref_kl.sum() / n)
+    assert torch.equal(loss.view(torch.int32), loss2.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    assert abs(loss.item() - ref_loss) <= LOSS_RTOL * abs(ref_loss), (loss.item(), ref_loss)
+    np.testing.assert_allclose(to_f64(lse), arrays["lse"][:n].astype(np.float64), rtol=LSE_RTOL)
+    np.testing.assert_allclose(to_f64(rows), ref_kl, rtol=LOSS_RTOL, atol=LOSS_RTOL)
+    print(f"[fullsize]   loss {loss.item():.6f} (oracle {ref_loss:.6f}); lse and KL of every row", flush=True)
+
+    W64 = kd_synth.to_float64(W, w.dtype)
+    if full_oracle:
+        H64 = kd_synth.to_float64(H, w.dtype)
+        v64 = kd_synth.to_float64(bf16_bits_of(val) if w.val_dtype == "bf16" else val.cpu().numpy(), w.val_dtype)
+        ref_dH, ref_dW = oracle.kl_backward(H64, W64, idx.cpu().numpy(), v64, w.tau, block=512)
+        e_dh, e_dw = chunked_rel_err(dh, ref_dH), chunked_rel_err(dw, ref_dW)
+        print(f"[fullsize]   every element: dH err {e_dh:.2e}, dW err {e_dw:.2e}", flush=True)
+        assert e_dh <= GRAD_TOL and e_dw <= GRAD_TOL
+        return
+    # dH on sampled rows (the oracle normalises by its own row count; rescale to 1/N)
+    rs = sample_rows(n, sample, seed=n + k)
     rs_t = torch.from_numpy(rs).to(device())
     H64 = kd_synth.to_float64(H[rs], w.dtype)
-    W64 = kd_synth.to_float64(W, w.dtype)
-    WT64 = kd_synth.to_float64(WT, w.dtype)
-    ref_idx, ref_val, _ = oracle.topk_cache(H64, WT64, k, w.val_dtype)
-    g_idx = idx[rs_t].cpu().numpy()
-    np.testing.assert_array_equal(g_idx, ref_idx)
-    g_val = val[rs_t]
-    if w.val_dtype == "bf16":
-        np.testing.assert_array_equal(bf16_bits_of(g_val), ref_val)
-    else:
-        np.testing.assert_array_equal(g_val.cpu().numpy().view(np.uint32), ref_val.view(np.uint32))
-
-    vref = kd_synth.to_float64(ref_val, w.val_dtype)
-    _, ref_lse, ref_rows = oracle.kl_forward(H64, W64, ref_idx, vref, w.tau)
-    np.testing.assert_allclose(to_f64(lse[rs_t]), ref_lse, rtol=LSE_RTOL)
-    np.testing.assert_allclose(to_f64(rows[rs_t]), ref_rows, rtol=LOSS_RTOL, atol=LOSS_RTOL)
-    # dH rows: the oracle normalises by its own row count; rescale to 1/N
-    ref_dH, _ = oracle.kl_backward(H64, W64, ref_idx, vref, w.tau)
+    ih = idx[rs_t].cpu().numpy()
+    vv = val[rs_t]
+    v64 = kd_synth.to_float64(bf16_bits_of(vv) if w.val_dtype == "bf16" else vv.cpu().numpy(), w.val_dtype)
+    ref_dH, _ = oracle.kl_backward(H64, W64, ih, v64, w.tau)
     ref_dH *= len(rs) / n
     assert rel_max_err(to_f64(dh[rs_t]), ref_dH) <= GRAD_TOL
-
-    # properties at any size
-    r_all = rows.double()
-    assert torch.isfinite(r_all).all() and (r_all >= -1e-4).all()
-    assert abs(r_all.mean().item() - loss.item()) <= 1e-5 * abs(loss.item())
     # Columns of dW sum to zero up to the bf16 rounding of dZ: each dZ row sums to
     # zero exactly, rounding moves each element by at most 2^-8 of its size, and
     # sum_v |dZ[t, v]| <= 2 / N, so |sum_v dW[v, j]| <= 2^-7 / N * sum_t |H[t, j]|.
@@ -79,62 +146,73 @@ def run_workload(name, n, k, rows_count=24, full_dw=False):
     bound = 2.0 ** -7 / n * h.double().abs().sum(0) * 1.01 + 2.0 ** -20 * dw64.abs().sum(0)
     assert bool((colsum <= bound).all()), float((colsum / bound).max())
     del dw64
-    if n > CHUNK:
-        # chunk additivity: dW over all N tokens equals the token-weighted sum of
-        # dW over each chunk alone (checks the cross-chunk accumulation)
-        acc = torch.zeros_like(dw, dtype=torch.float64)
-        for c0 in range(0, n, CHUNK):
-            c1 = min(n, c0 + CHUNK)
-            hc, ic, vc = h[c0:c1].contiguous(), idx[c0:c1].contiguous(), val[c0:c1].contiguous()
-            _, lc, _ = kd.kd_chunked_kl_fwd(hc, wd, ic, vc, w.tau)
-            _, dwc = kd.kd_chunked_kl_bwd(hc, wd, ic, vc, w.tau, lc, None, dh_dtype=torch.float32)
-            acc += dwc.double() * ((c1 - c0) / n)
-            del dwc
-        torch.cuda.synchronize()
-        assert (acc - dw.double()).abs().max().item() <= 1e-4 * dw.abs().max().item()
-        del acc
-
-    if full_dw:
-        # Every element: the oracle builds its own cache for all rows; the GPU
-        # cache must equal it, and the GPU loss and gradients are recomputed on
-        # the oracle's cache bytes.
-        Hall = kd_synth.to_float64(H, w.dtype)
-        oi, ov, _ = oracle.topk_cache(Hall, WT64, k, w.val_dtype)
-        np.testing.assert_array_equal(idx.cpu().numpy(), oi)
-        ref_loss, ref_lse_all, _ = oracle.kl_forward(Hall, W64, oi, kd_synth.to_float64(ov, w.val_dtype), w.tau)
-        ref_dH_all, ref_dW = oracle.kl_backward(Hall, W64, oi, kd_synth.to_float64(ov, w.val_dtype), w.tau)
-        ti, tv = torch.from_numpy(oi).to(device()), to_dev(ov, w.val_dtype)
-        loss2, lse2, _ = kd.kd_chunked_kl_fwd(h, wd, ti, tv, w.tau)
-        dh2, dw2 = kd.kd_chunked_kl_bwd(h, wd, ti, tv, w.tau, lse2, None, dh_dtype=torch.float32)
-        torch.cuda.synchronize()
-        assert abs(loss2.item() - ref_loss) <= LOSS_RTOL * abs(ref_loss)
-        np.testing.assert_allclose(to_f64(lse2), ref_lse_all, rtol=LSE_RTOL)
-        assert rel_max_err(to_f64(dh2), ref_dH_all) <= GRAD_TOL
-        assert rel_max_err(to_f64(dw2), ref_dW) <= GRAD_TOL
-    return loss.item()
+    print(f"[fullsize]   dH on {len(rs)} sampled rows; dW column sums", flush=True)
+    return h, wd, idx, val, dw
 
 
-def test_seq4k_v32k_full():
-    """4,096 tokens, d=2048, V=32,000, K=100: every output element checked,
-    including the whole teacher cache and dW."""
-    run_workload("seq4k_v32k", 4096, 100, rows_count=32, full_dw=True)
+def test_seq4k_v32k():
+    """4,096 tokens, d=2048, V=32,000, K=100 (split-K dH)."""
+    run_workload("seq4k_v32k", 4096, 100, full_oracle=True)
 
 
+@pytest.mark.timeout(900)
 def test_long32k_v201k():
-    run_workload("long32k_v201k", 32768, 100)
+    """32,768 tokens, d=2880, V=201,088: every element of dH and dW."""
+    run_workload("long32k_v201k", 32768, 100, full_oracle=True)
 
 
+@pytest.mark.timeout(900)
 def test_ctx32k_v128k():
-    run_workload("ctx32k_v128k", 32768, 100)
+    """32,768 tokens at V=128,256, d=4,096: the point where half of MFMA peak is
+    asked for; every element of dH and dW."""
+    run_workload("ctx32k_v128k", 32768, 100, full_oracle=True)
 
 
+@pytest.mark.timeout(600)
 def test_packed131k_v128k():
-    run_workload("packed131k_v128k", 131072, 100, rows_count=16)
+    """131,072 tokens, tau = 2, independent teacher: the benchmark's default
+    workload.  Also chunk additivity of dW over the eight 16K-token chunks."""
+    h, wd, idx, val, dw = run_workload("packed131k_v128k", 131072, 100, full_oracle=False)
+    w = kd_synth.WORKLOADS["packed131k_v128k"]
+    n = h.shape[0]
+    acc = torch.zeros_like(dw, dtype=torch.float64)
+    for c0 in range(0, n, CHUNK):
+        c1 = min(n, c0 + CHUNK)
+        hc, ic, vc = h[c0:c1].contiguous(), idx[c0:c1].contiguous(), val[c0:c1].contiguous()
+        _, lc, _ = kd.kd_chunked_kl_fwd(hc, wd, ic, vc, w.tau)
+        _, dwc = kd.kd_chunked_kl_bwd(hc, wd, ic, vc, w.tau, lc, None, dh_dtype=torch.bfloat16)
+        acc += dwc.double() * ((c1 - c0) / n)
+        del dwc
+    torch.cuda.synchronize()
+    assert (acc - dw.double()).abs().max().item() <= 1e-4 * dw.abs().max().item()
 
 
-@pytest.mark.parametrize("n,k", [(4096, 50), (4096, 500), (262144, 100)])
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("n,k", [(4096, 50), (4096, 500), (16384, 50), (16384, 500), (65536, 100),
+                                 (262144, 100)])
 def test_sweep_points(n, k):
-    run_workload("sweep_v128k", n, k, rows_count=12)
+    run_workload("sweep_v128k", n, k, full_oracle=False, sample=32)
+
+
+@pytest.mark.timeout(900)
+def test_sweep_16k_full():
+    """16,384 tokens of the sweep at K = 100: every element of dH and dW."""
+    run_workload("sweep_v128k", 16384, 100, full_oracle=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("k", [50, 500])
+def test_sweep_262k_cache(k):
+    """The teacher cache of all 262,144 sweep tokens at K = 50 and K = 500, every row."""
+    w = kd_synth.WORKLOADS["sweep_v128k"]
+    meta, _ = golden("sweep_v128k")
+    n = 262144
+    print(f"[fullsize] sweep_v128k cache N={n} K={k}", flush=True)
+    h = to_dev(kd_synth.hidden(w, n), w.dtype)
+    wt = to_dev(kd_synth.teacher_head(w), w.dtype)
+    idx, val = kd.kd_topk_cache_build(h, wt, k)
+    torch.cuda.synchronize()
+    check_cache(idx, val, meta, k, n)
 
 
 def test_peak_memory_linear_in_tokens():
@@ -196,7 +274,7 @@ def test_loss_options_ctx32k_v128k():
     h, wd = to_dev(H, w.dtype), to_dev(W, w.dtype)
     ti, tv, tl = torch.from_numpy(idx).to(device()), to_dev(valb, "bf16"), torch.from_numpy(labels).to(device())
     loss, lse, rows = kd.kd_chunked_kl_fwd(h, wd, ti, tv, w.tau, with_rows=True, labels=tl, ce_weight=a)
-    dh, dw = kd.kd_chunked_kl_bwd(h, wd, ti, tv, w.tau, lse, None, dh_dtype=torch.float32, labels=tl, ce_weight=a)
+    dh, dw = kd.kd_chunked_kl_bwd(h, wd, ti, tv, w.tau, lse, None, dh_dtype=torch.bfloat16, labels=tl, ce_weight=a)
     torch.cuda.synchronize()
 
     count = int((labels != ign).sum())

@@ -88,6 +88,15 @@ class ClockSampler:
             self.handle = None
 
     def _read(self):
+        # the per-XCD graphics clocks of the GPU metrics table, averaged; else the
+        # clock query's single value
+        try:
+            m = self._amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+            xs = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 5000]
+            if xs:
+                return sum(xs) / len(xs)
+        except Exception:
+            pass
         c = self._amdsmi.amdsmi_get_clock_info(self.handle, self._amdsmi.AmdSmiClkType.GFX)
         return float(c["clk"])
 
@@ -486,8 +495,13 @@ def measure(kd, torch, w, h, wd, idx, val, n, k, steps, warmup, chunk, clock):
     peak_tf = BF16_DENSE_PEAK_TFLOPS if w.dtype == "bf16" else FP32_DENSE_PEAK_TFLOPS
     mfma_util = flops_step / (ms / 1e3) / (peak_tf * 1e12)
     mid = per_step[len(per_step) // 2] if steps % 2 else 0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2])
+    # utilisation against the peak at the clock measured meanwhile (the peak scales with
+    # it); a reading that would put the MFMA pipes above their peak is not a clock the
+    # kernels ran at (e.g. under a profiler), and is dropped
+    if clk is not None and mfma_util * 2400.0 / clk[0] > 1.0:
+        log(f"clock samples ({clk[0]:.0f} MHz) inconsistent with the measured throughput; not reported")
+        clk = None
     clock_mhz = None if clk is None else round(clk[0], 1)
-    # utilisation against the peak at the clock measured meanwhile (the peak scales with it)
     util_clk = None if clk is None else round(mfma_util * 2400.0 / clk[0], 4)
     log(f"{steps} steps: {ms:.2f} ms/step (median {mid:.2f}, min {per_step[0]:.2f}), {n / (ms / 1e3):.0f} tokens/s, "
         f"MFMA {100 * mfma_util:.1f}% of dense peak at 2.4 GHz"

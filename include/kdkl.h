@@ -125,13 +125,17 @@ typedef struct {
 kd_status kd_workspace_size(kd_op op, const kd_problem* p, size_t* bytes);
 
 /* Offline teacher cache ([abs]; [wiki] "핵심 아이디어 1", "사전 계산 파이프라인"):
- * S = H_T W_T^T evaluated tile by tile with bf16 (or f32) MFMA, then an exact
- * per-row top-K. Candidates within a rigorous float32 error bound of the K-th
- * value are re-scored in float64, so the chosen set and order equal those of the
- * exact logits. Output rows are sorted by exact logit, descending; equal logits
- * put the smaller index first.
+ * S = H_T W_T^T evaluated tile by tile with bf16 (or f32) MFMA, then a per-row
+ * top-K. Every logit within a rigorous float32 error bound of the K-th value is
+ * re-scored in float64: the products of bf16 (or f32) inputs are exact in float64
+ * and are summed in a fixed order, each addition rounded to float64. Rows are
+ * ranked by that float64 score, descending, equal scores putting the smaller index
+ * first. So the chosen set and order are those of the exact logits wherever the
+ * exact logits of two candidates differ by more than the float64 summation error
+ * (at most about d 2^-53 sum_j |h_j w_j|); closer than that, the float64 scores
+ * decide (and may tie).
  *   h_t   [N, d] x_dtype          w_t [V, d] x_dtype
- *   idx_out [N, K] int32          val_out [N, K] val_dtype: the exact logit rounded
+ *   idx_out [N, K] int32          val_out [N, K] val_dtype: the float64 score rounded
  *                                 once (nearest, ties to even) to bf16 / f32.
  * A row with more than 6,144 logits within the error bound of its K-th value (a
  * massive near-tie, e.g. thousands of identical teacher rows at the top) exceeds

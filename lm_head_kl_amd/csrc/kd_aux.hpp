@@ -797,8 +797,9 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, int need, int* 
 //  2. Every value >= lo - 2*eps is a candidate, where eps bounds |fp32 - exact|
 //     for any logit of the row (Higham's summation bound with Cauchy-Schwarz:
 //     eps = 2 d 2^-23 ||h|| max_v ||w_v||).  Every exact top-K member is in the set.
-//  3. Candidates are re-scored exactly-rounded in float64, ranked by (score desc,
-//     index asc), and the first K are written.
+//  3. Candidates are re-scored in float64 (exact products, a fixed summation order,
+//     each addition rounded to float64), ranked by (score desc, index asc), and the
+//     first K are written.
 template <typename T, typename VT>
 __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
     const float* __restrict__ S, int64_t ld_s, int V, int K, const T* __restrict__ ht, int d,

@@ -363,6 +363,43 @@ def test_topk_exact_ties_take_the_smaller_index(dtype):
     assert (gi_np[:, 0:50:2] + 1500 == gi_np[:, 1:50:2]).all() and (gi_np[:, 50] < 1500).all()
 
 
+def test_topk_near_ties_below_float64_resolution():
+    """Exact logits closer than float64 can resolve: every row's top 16 logits are
+    2^40 + s c_v 2^-20 (c_v = 1..16, s = +1 on even rows, -1 on odd rows), all of
+    which sum to exactly 2^40 in float64, and the other 48 are near 2^39.  Both the
+    GPU's float64 re-score and the oracle's float64 product see 16 equal scores and
+    keep the smaller indices, bit for bit alike; on even rows the exact order is the
+    reverse (it differs from the float64 order only within the summation error
+    bound, d 2^-53 sum_j |h_j w_j|)."""
+    from fractions import Fraction
+    n, d, v, k = 4, 8, 64, 8
+    h = np.zeros((n, d), np.float32)
+    h[:, 0] = 2.0 ** 20
+    h[:, 1] = [(1 if i % 2 == 0 else -1) * 2.0 ** -20 for i in range(n)]
+    wt = np.zeros((v, d), np.float32)
+    wt[:16, 0] = 2.0 ** 20
+    wt[16:, 0] = 2.0 ** 19
+    wt[:, 1] = (np.arange(v) % 16) + 1
+    hb, wb = kd_synth.bf16_bits_from_f32(h), kd_synth.bf16_bits_from_f32(wt)
+    assert np.array_equal(kd_synth.f32_from_bf16_bits(hb), h) and np.array_equal(kd_synth.f32_from_bf16_bits(wb), wt)
+    ref_idx, ref_val, ref_sc = oracle.topk_cache(h.astype(np.float64), wt.astype(np.float64), k, "bf16")
+    gi, gv = kd.kd_topk_cache_build(to_dev(hb, "bf16"), to_dev(wb, "bf16"), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gi.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(bf16_bits_of(gv), ref_val)
+    assert (ref_sc == 2.0 ** 40).all() and (ref_idx == np.arange(k)).all()
+    for i in range(n):
+        exact = [sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(h[i], wt[u])) for u in range(v)]
+        order = sorted(range(v), key=lambda u: (-exact[u], u))[:k]
+        if i % 2 == 0:
+            assert order == list(range(15, 15 - k, -1))          # the exact order differs ...
+        else:
+            assert order == list(range(k))
+        bound = d * 2.0 ** -53 * float(sum(abs(Fraction(float(a)) * Fraction(float(b))) for a, b in zip(h[i], wt[0])))
+        kth = sorted(exact, reverse=True)[k - 1]
+        assert all(float(kth - exact[u]) <= bound for u in ref_idx[i])   # ... only within the bound
+
+
 def test_uninformed_student_closed_form():
     """W = 0: every student logit is 0, so lse = log V exactly, KL_i = sum_k p log p +
     log V (a closed form, no oracle needed), dH = dZ W = 0 exactly and dW = dZ^T H

@@ -658,49 +658,117 @@ __global__ void __launch_bounds__(256) renorm_dh_kernel(const T* __restrict__ w,
   }
 }
 
-// dZ[t][idx[t][k]] += c[t][k] on a zeroed dZ chunk (and dZ^T when that copy
-// exists), so that the dW product runs on it.  RB_ROWS rows per block, RB_TPR
-// threads per row; entries are applied in batches of RB_TPR in k order: within a
-// batch, repeated indices are summed (in k order) by their first occurrence, and a
-// block barrier orders the batches, so every element is updated by one thread at a
-// time and repeated indices accumulate in a fixed order.
+// dW of the renormalised student, whose dZ is zero off the cached entries:
+//   dW[v] (+)= sum over the chunk's entries with index v of c * H[t]
+// from the chunk's entries bucketed per (256-token, 256-vocabulary) tile in a fixed
+// order, with their gradients c beside them.  One block per vocabulary tile, each wave
+// one vocabulary row at a time: the row's entries are collected in order (token tiles
+// ascending, then the bucket's order) into the wave's LDS list, up to RDW_LIST at a
+// time, and applied in that order to 8 columns per lane; a row with more entries goes
+// through its dW row in pieces (float32 partial sums through memory, the same order).
+// Rows without entries are written as 0, or left as they are when accumulating.
+constexpr int RDW_LIST = 1024;
 template <typename T>
-__global__ void __launch_bounds__(256) renorm_scatter_kernel(const int32_t* __restrict__ idx,
-                                                             const float* __restrict__ c, int nr, int kc, int vocab,
-                                                             const int32_t* __restrict__ labels, int ignore,
-                                                             T* __restrict__ dz, int64_t ldz, T* __restrict__ dzt,
-                                                             int64_t ldzt) {
-  __shared__ int bidx[RB_ROWS][RB_TPR];
-  __shared__ float bc[RB_ROWS][RB_TPR];
-  const int r = threadIdx.x & (RB_ROWS - 1), q = threadIdx.x / RB_ROWS;
-  const int t = blockIdx.x * RB_ROWS + r;
-  const bool counted = t < nr && (labels == nullptr || labels[t] != ignore);
-  for (int k0 = 0; k0 < kc; k0 += RB_TPR) {
-    const int k = k0 + q;
-    int v = -1;
-    float ck = 0.f;
-    if (counted && k < kc) {
-      v = idx[(int64_t)t * kc + k];
-      if ((unsigned)v >= (unsigned)vocab) v = -1;
-      else ck = c[(int64_t)t * kc + k];
-    }
-    bidx[r][q] = v;
-    bc[r][q] = ck;
-    __syncthreads();
-    bool first = v >= 0;
-    for (int j = 0; j < q && first; ++j) first = bidx[r][j] != v;
-    if (first) {
-      float sum = ck;
-      for (int j = q + 1; j < RB_TPR; ++j)
-        if (bidx[r][j] == v) sum += bc[r][j];
-      T* a = dz + (int64_t)t * ldz + v;
-      *a = from_f32<T>(to_f32<T>(*a) + sum);
-      if (dzt) {
-        T* b = dzt + (int64_t)v * ldzt + t;
-        *b = from_f32<T>(to_f32<T>(*b) + sum);
+__global__ void __launch_bounds__(256) renorm_dw_kernel(const uint32_t* __restrict__ entries,
+                                                        const float* __restrict__ ew, const int* __restrict__ offsets,
+                                                        int n_tx, int n_ty, int kz, const T* __restrict__ h, int d,
+                                                        int vocab, int accumulate, float* __restrict__ dw) {
+  __shared__ int lt[4][RDW_LIST];
+  __shared__ float lc[4][RDW_LIST];
+  const int ty = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int* mt = lt[wave];
+  float* mc = lc[wave];
+  for (int vl = wave; vl < 256; vl += 4) {
+    const int v = ty * 256 + vl;
+    if (v >= vocab) break;
+    float* out = dw + (int64_t)v * d;
+    int tx = 0;
+    int e = offsets[ty], ee = offsets[ty + 1];
+    bool first = true, done = false;
+    while (!done) {
+      // collect the next RDW_LIST entries of this row, in order
+      int n = 0;
+      while (true) {
+        while (e >= ee && tx + 1 < n_tx) {
+          ++tx;
+          e = offsets[(int64_t)tx * (n_ty + 1) + ty];
+          ee = offsets[(int64_t)tx * (n_ty + 1) + ty + 1];
+        }
+        if (e >= ee) {
+          done = true;
+          break;
+        }
+        const int q = e + lane;
+        bool m = false;
+        uint32_t u = 0;
+        if (q < ee) {
+          u = entries[(int64_t)tx * BX * kz + q];
+          m = int((u >> 8) & 255u) == vl;
+        }
+        const uint64_t bm = __ballot(m);
+        const int cnt = __builtin_popcountll(bm);
+        if (n + cnt > RDW_LIST) break;     // the list is full: apply it, then resume here
+        if (m) {
+          const int pos = n + lane_rank(bm);
+          mt[pos] = tx * BX + int(u & 255u);
+          mc[pos] = ew[(int64_t)tx * BX * kz + q];
+        }
+        n += cnt;
+        e = min(e + 64, ee);
       }
+      wave_sync_lds();
+      if (n > 0 || (first && !accumulate)) {
+        for (int j0 = lane * 8; j0 - lane * 8 < d; j0 += 512) {
+          const bool jin = j0 < d;
+          float acc[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[x] = 0.f;
+          if (jin && (!first || accumulate)) {
+            const f32x4 a = *(const f32x4*)(out + j0), b = *(const f32x4*)(out + j0 + 4);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              acc[x] = a[x];
+              acc[4 + x] = b[x];
+            }
+          }
+          for (int q0 = 0; q0 < n; q0 += 16) {
+            const int qn = min(16, n - q0);
+            u32x4 hv[16][sizeof(T) == 2 ? 1 : 2];
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+              if (q < qn && jin) {
+                const T* hr = h + (int64_t)mt[q0 + q] * d + j0;
+                hv[q][0] = *(const u32x4*)hr;
+                if constexpr (sizeof(T) == 4) hv[q][sizeof(T) == 2 ? 0 : 1] = *(const u32x4*)(hr + 4);
+              }
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+              if (q < qn && jin) {
+                const float c = mc[q0 + q];
+                if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                  for (int x = 0; x < 4; ++x) {
+                    acc[2 * x] = fmaf(c, __uint_as_float(hv[q][0][x] << 16), acc[2 * x]);
+                    acc[2 * x + 1] = fmaf(c, __uint_as_float(hv[q][0][x] & 0xffff0000u), acc[2 * x + 1]);
+                  }
+                } else {
+#pragma unroll
+                  for (int x = 0; x < 4; ++x) {
+                    acc[x] = fmaf(c, __uint_as_float(hv[q][0][x]), acc[x]);
+                    acc[4 + x] = fmaf(c, __uint_as_float(hv[q][sizeof(T) == 2 ? 0 : 1][x]), acc[4 + x]);
+                  }
+                }
+              }
+          }
+          if (jin) {
+            *(f32x4*)(out + j0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            *(f32x4*)(out + j0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+          }
+        }
+      }
+      first = false;
+      wave_sync_lds();   // the list is read before the next piece overwrites it
     }
-    __syncthreads();   // this batch's updates before the next batch's reads
   }
 }
 

@@ -483,18 +483,16 @@ kd_status run_dh(const GemmArgs& g, bool w_kmajor, int64_t out_bytes, hipStream_
 // Backward with the student renormalised over the cached entries.  dZ is zero off
 // each row's cached entries: per chunk the logits at the entries again (gather_dot),
 // their gradient c = (g/N)(q - p), dH by a gather of W rows weighted by c, and dW by
-// the dW product on a dZ chunk that holds c at the cached entries and zeros
-// elsewhere (the same product, and summation order, as the full backward).
+// each vocabulary row's sum of c H[t] over its entries, in a fixed order.
 template <typename T>
 kd_status bwd_renorm_impl(const Plan& pl, const Layout& L, const void* h, const void* w, const int32_t* idx,
                           const void* val, const float* lse, const float* grad, void* dh, float* dw, char* ws,
                           hipStream_t st, const Opts& o) {
-  constexpr bool kKm = std::is_same<T, bf16_t>::value;
-  T* ht = (T*)(ws + L.ht);
-  T* dz = (T*)(ws + L.dz);
-  T* dzt = kKm ? nullptr : (T*)(ws + L.dzt);
   float* zg = (float*)(ws + L.ew);
   float* cf = (float*)(ws + L.pw);
+  uint32_t* entries = (uint32_t*)(ws + L.entries);
+  int* offsets = (int*)(ws + L.offsets);
+  int* flags = (int*)(ws + L.flags);
   float inv_n = 1.0f / (float)pl.N;
   const float inv_tau = 1.0f / pl.tau;
   const int64_t es = (int64_t)sizeof(T);
@@ -505,7 +503,6 @@ kd_status bwd_renorm_impl(const Plan& pl, const Layout& L, const void* h, const 
   }
   for (int64_t r0 = 0; r0 < pl.N; r0 += pl.Nc) {
     const int nr = (int)std::min<int64_t>(pl.Nc, pl.N - r0);
-    const int nr64 = (int)round_up(nr, 64);
     const T* hc = (const T*)h + r0 * pl.d;
     const int32_t* idx_c = idx + r0 * pl.K;
     const int32_t* lab_c = o.labels ? o.labels + r0 : nullptr;
@@ -530,26 +527,15 @@ kd_status bwd_renorm_impl(const Plan& pl, const Layout& L, const void* h, const 
         hipLaunchKernelGGL((renorm_dh_kernel<T, bf16_t>), dim3(nr), dim3(256), 0, st, (const T*)w, idx_c, cf, nr,
                            pl.K, (int)pl.d, (int)pl.V, lab_c, o.ignore, (bf16_t*)dh + r0 * pl.d);
     }));
-    // dZ chunk: zeros, then c at the cached entries
-    KD_TRY(zero_words(dz, es * nr64 * pl.ld_v / 4, st));
-    if (dzt) KD_TRY(zero_words(dzt, es * pl.V_pad * pl.ld_t / 4, st));
-    KD_TRY(launch("renorm_scatter", 0.0, (double)nr * pl.K * (8.0 + 2.0 * es), st, [&] {
-      hipLaunchKernelGGL(renorm_scatter_kernel<T>, dim3(nb), dim3(256), 0, st, idx_c, cf, nr, pl.K, (int)pl.V, lab_c,
-                         o.ignore, dz, pl.ld_v, dzt, pl.ld_t);
+    // dW: the entries with their gradients, bucketed per tile in a fixed order (the
+    // gathered logits are no longer needed, so their buffer takes the weights), then
+    // each vocabulary row's sum over its entries
+    KD_TRY(run_bucket(pl, idx_c, lab_c, o, 0, nr, pl.K, true, cf, entries, zg, offsets, flags, st));
+    KD_TRY(launch("renorm_dw", 2.0 * nr * pl.K * (double)pl.d, (double)nr * pl.K * es * pl.d + 4.0 * pl.V * pl.d, st,
+                  [&] {
+      hipLaunchKernelGGL(renorm_dw_kernel<T>, dim3((unsigned)pl.n_ty), dim3(256), 0, st, entries, zg, offsets,
+                         (int)cdiv(nr, BX), pl.n_ty, pl.K, hc, (int)pl.d, (int)pl.V, r0 > 0 ? 1 : 0, dw);
     }));
-    KD_TRY(launch("transpose_h", 0.0, 2.0 * es * nr * pl.d, st, [&] {
-      hipLaunchKernelGGL(transpose_pad_kernel<T>, dim3((unsigned)cdiv(nr64, 64), (unsigned)cdiv(pl.d, 64)),
-                         dim3(256), 0, st, hc, pl.d, nr, (int)pl.d, ht, pl.ld_t, nr64);
-    }));
-    GemmArgs gw = kKm ? gemm_args(dz, pl.ld_v, (int)pl.V, ht, pl.ld_t, (int)pl.d, nr64)
-                      : gemm_args(dzt, pl.ld_t, (int)pl.V, ht, pl.ld_t, (int)pl.d, nr64);
-    gw.krows_x = nr;
-    gw.out = dw;
-    gw.ldo = pl.d;
-    gw.out_rows = (int)pl.V;
-    gw.out_cols = (int)pl.d;
-    gw.accumulate = r0 > 0;
-    KD_TRY((run_gemm<T, EPI_STORE_F32, kKm, 0>("gemm_dw", gw, (r0 > 0 ? 8 : 4) * pl.V * pl.d, st)));
   }
   return KD_OK;
 }

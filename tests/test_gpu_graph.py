@@ -82,3 +82,37 @@ def test_graph_replays_equal_eager(with_options):
     for a, b in zip(out, ref2):
         assert torch.equal(a, b)
     assert not torch.equal(ref2[2], ref[2])
+
+
+@pytest.mark.parametrize("student", ["full", "renorm"])
+def test_graph_noalloc_forward(student):
+    """The allocation-free forward under capture (the case it exists for: nothing to
+    allocate while capturing), with the padding mask and both student normalisers:
+    every replay equals the forward with a caller's workspace, bit for bit."""
+    n, d, v, k, tau = 3000, 128, 5000, 16, 1.3
+    print(f"[case] graph noalloc student={student}", flush=True)
+    h, w, wt, lab = _static_inputs(n, d, v, seed=53)
+    idx, val = kd.kd_topk_cache_build(h, wt, k)
+    ref_loss, ref_lse, ref_rows = kd.kd_chunked_kl_fwd(h, w, idx, val, tau, with_rows=True, labels=lab,
+                                                       student=student)
+    loss = torch.empty((), dtype=torch.float32, device=device())
+    lse = torch.empty((n,), dtype=torch.float32, device=device())
+    rows = torch.empty((n,), dtype=torch.float32, device=device())
+    kd.kd_chunked_kl_fwd_noalloc(h, w, idx, val, tau, loss, lse, rows, labels=lab, student=student)   # eager
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kd.kd_chunked_kl_fwd_noalloc(h, w, idx, val, tau, loss, lse, rows, labels=lab, student=student)
+    torch.cuda.synchronize()
+    for r in range(3):
+        loss.zero_()
+        lse.zero_()
+        rows.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss.view(torch.int32), ref_loss.view(torch.int32)), f"replay {r}"
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
+        assert torch.equal(rows.view(torch.int32), ref_rows.view(torch.int32))
+        e, _, _ = kd.kd_chunked_kl_fwd(h, w, idx, val, tau, labels=lab, student=student)   # eager work between
+        torch.cuda.synchronize()
+        assert torch.equal(e, ref_loss)

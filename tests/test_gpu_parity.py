@@ -100,6 +100,43 @@ def test_topk_selection_paths(case):
     np.testing.assert_array_equal(bf16_bits_of(gv), val)
 
 
+@pytest.mark.parametrize("case", [
+    # (N, d, V, K, dtype): the float64 re-scoring walks a row in steps of 4,096 (bf16)
+    # or 2,048 (float32) elements: one full step, and a second ragged one
+    (40, 4096, 3000, 20, "bf16"),
+    (40, 4104, 3000, 20, "bf16"),
+    (40, 2048, 3000, 20, "f32"),
+    (40, 2056, 3000, 20, "f32"),
+], ids=lambda c: "x".join(map(str, c)))
+def test_topk_rescoring_at_wide_hidden_rows(case):
+    """The re-scoring's step boundary, at and just past it; bit-exact idx and val."""
+    n, d, v, k, dtype = case
+    p, H, W, WT, idx, val = _problem(n, d, v, k, dtype, seed=21)
+    gi, gv = kd.kd_topk_cache_build(to_dev(p["H"], dtype), to_dev(p["WT"], dtype), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gi.cpu().numpy(), idx)
+    if dtype == "bf16":
+        np.testing.assert_array_equal(bf16_bits_of(gv), val)
+    else:
+        np.testing.assert_array_equal(gv.cpu().numpy().view(np.uint32), val.view(np.uint32))
+
+
+def test_topk_rows_sharing_every_candidate():
+    """Half the rows share one hidden state, so every one of them has the same
+    candidates and the same near-ties; the other rows interleave with their own."""
+    n, d, v, k = 300, 64, 5000, 40
+    p = kd_synth.small_problem(n, d, v, seed=22)
+    p["H"][1::2] = p["H"][0]        # half the rows equal row 0, the rest their own
+    H = kd_synth.to_float64(p["H"], "bf16")
+    WT = kd_synth.to_float64(p["WT"], "bf16")
+    idx, val, _ = oracle.topk_cache(H, WT, k, "bf16")
+    assert (idx[1::2] == idx[0]).all()
+    gi, gv = kd.kd_topk_cache_build(to_dev(p["H"], "bf16"), to_dev(p["WT"], "bf16"), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gi.cpu().numpy(), idx)
+    np.testing.assert_array_equal(bf16_bits_of(gv), val)
+
+
 @pytest.mark.parametrize("scale", [8.0, 30.0])
 def test_large_logit_scale(scale):
     """Stress variant: logits ~ N(0, scale^2) (row maxima near 4 scale), so the

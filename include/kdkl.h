@@ -125,9 +125,11 @@ typedef struct {
 kd_status kd_workspace_size(kd_op op, const kd_problem* p, size_t* bytes);
 
 /* Offline teacher cache ([abs]; [wiki] "핵심 아이디어 1", "사전 계산 파이프라인"):
- * S = H_T W_T^T evaluated tile by tile with bf16 (or f32) MFMA, then a per-row
- * top-K. Every logit within a rigorous float32 error bound of the K-th value is
- * re-scored in float64: the products of bf16 (or f32) inputs are exact in float64
+ * S = H_T W_T^T evaluated tile by tile with bf16 (or f32) MFMA and float32
+ * accumulation (kept in the workspace rounded to bf16, beside each row's two
+ * largest float32 logits per 256-column tile), then a per-row top-K. Every logit
+ * within a rigorous float32 error bound of the K-th value (widened by the bf16
+ * rounding of the kept logits) is re-scored in float64: the products of bf16 (or f32) inputs are exact in float64
  * and are summed in a fixed order, each addition rounded to float64. Rows are
  * ranked by that float64 score, descending, equal scores putting the smaller index
  * first. So the chosen set and order are those of the exact logits wherever the

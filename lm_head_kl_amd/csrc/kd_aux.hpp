@@ -829,6 +829,24 @@ __global__ void __launch_bounds__(256) max_reduce_kernel(const double* __restric
   if (threadIdx.x == 0) *out = sh[0];
 }
 
+// The largest bfloat16 value <= x (x a finite float, not NaN).
+__device__ __forceinline__ float bf16_floor(float x) {
+  const uint32_t t = __float_as_uint(x) & 0xffff0000u;     // toward zero
+  float b = __uint_as_float(t);
+  if (b > x) b = __uint_as_float(t + 0x10000u);            // negative x: one bf16 step down
+  return b;
+}
+
+// The logits are stored rounded to bfloat16 (nearest even), a monotone map, so a
+// stored value s is the rounding of a float32 logit x with x >= s - max(2^-8 |s|,
+// 2^-133): half a bfloat16 unit in the last place is at most 2^-8 |s| for a normal
+// s and 2^-134 below.  That bound is increasing in s, so it maps a lower bound of
+// a stored value to a lower bound of its logit.
+__device__ __forceinline__ double bf16_logit_lower(float s) {
+  const double a = fabs((double)s) * 0x1p-8;
+  return (double)s - (a > 0x1p-133 ? a : 0x1p-133);
+}
+
 constexpr int SEL_CAP = 6144;    // candidate capacity per row (K <= 4096)
 constexpr int SEL_THREADS = 256;
 
@@ -859,18 +877,22 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, int need, int* 
 }
 
 // Exact top-K of one teacher row (general path; with rows_todo, only the rows the
-// fast path below handed over).  s[V] holds the float32 MFMA logits.
+// fast path below handed over).  s[V] holds the float32 MFMA logits rounded to
+// bfloat16.
 //  1. Two 12-bit radix histograms of the order-preserving key locate a
-//     sub-bin [lo, ...) that contains the K-th largest float32 value T_K.
-//  2. Every value >= lo - 2*eps is a candidate, where eps bounds |fp32 - exact|
+//     sub-bin [lo, ...) that contains the K-th largest stored value S_K; the K-th
+//     largest float32 logit is >= bf16_logit_lower(lo) =: T.
+//  2. Every logit >= T - 2*eps is a candidate, where eps bounds |fp32 - exact|
 //     for any logit of the row (Higham's summation bound with Cauchy-Schwarz:
-//     eps = 2 d 2^-23 ||h|| max_v ||w_v||).  Every exact top-K member is in the set.
+//     eps = 2 d 2^-23 ||h|| max_v ||w_v||); the rounding is monotone, so every
+//     such logit is stored as a value >= bf16_floor(T - 2*eps).  Every exact
+//     top-K member is in the set.
 //  3. Candidates are re-scored in float64 (exact products, a fixed summation order,
 //     each addition rounded to float64), ranked by (score desc, index asc), and the
 //     first K are written.
 template <typename T, typename VT>
 __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
-    const float* __restrict__ S, int64_t ld_s, int V, int K, const T* __restrict__ ht, int d,
+    const bf16_t* __restrict__ S, int64_t ld_s, int V, int K, const T* __restrict__ ht, int d,
     const T* __restrict__ wt, const double* __restrict__ wmax, int32_t* __restrict__ idx_out,
     VT* __restrict__ val_out, int* __restrict__ overflow, const int* __restrict__ rows_todo) {
   if (rows_todo && !rows_todo[blockIdx.x]) return;   // handled by topk_select_fast_kernel
@@ -880,7 +902,7 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
   __shared__ int sh[40];
   __shared__ double shd[SEL_THREADS];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* s = S + (int64_t)row * ld_s;
+  const bf16_t* s = S + (int64_t)row * ld_s;
   const T* h = ht + (int64_t)row * d;
 
   // ||h||_2 in float64
@@ -895,7 +917,7 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
   // pass 1: top 12 bits of the key
   for (int b = tid; b < 4096; b += SEL_THREADS) hist[b] = 0u;
   __syncthreads();
-  for (int v = tid; v < V; v += SEL_THREADS) atomicAdd(&hist[float_key(s[v]) >> 20], 1u);
+  for (int v = tid; v < V; v += SEL_THREADS) atomicAdd(&hist[float_key(bf16_to_f32(s[v])) >> 20], 1u);
   __syncthreads();
   select_bin(hist, K, sh, sh + 34);
   const uint32_t B = (uint32_t)sh[34];
@@ -905,19 +927,19 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
   for (int b = tid; b < 4096; b += SEL_THREADS) hist[b] = 0u;
   __syncthreads();
   for (int v = tid; v < V; v += SEL_THREADS) {
-    const uint32_t key = float_key(s[v]);
+    const uint32_t key = float_key(bf16_to_f32(s[v]));
     if ((key >> 20) == B) atomicAdd(&hist[(key >> 8) & 0xfffu], 1u);
   }
   __syncthreads();
   select_bin(hist, K - above, sh, sh + 36);
   const uint32_t B2 = (uint32_t)sh[36];
   const float lo = key_float((B << 20) | (B2 << 8));
-  const float thr = __double2float_rd((double)lo - 2.0 * eps);
+  const float thr = bf16_floor(__double2float_rd(bf16_logit_lower(lo) - 2.0 * eps));
   if (tid == 0) sh[38] = 0;
   __syncthreads();
   // pass 3: candidates
   for (int v = tid; v < V; v += SEL_THREADS) {
-    if (s[v] >= thr) {
+    if (bf16_to_f32(s[v]) >= thr) {
       const int pos = atomicAdd(&sh[38], 1);
       if (pos < SEL_CAP) cidx[pos] = v;
     }
@@ -956,13 +978,14 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
 }
 
 // Exact top-K of one teacher row, fast path.  The GEMM epilogue left, for every
-// 256-column vocabulary tile, the row's two largest float32 logits in the tile.
+// 256-column vocabulary tile, the row's two largest float32 logits in the tile
+// (before the logits' rounding to bfloat16).
 //  1. Those 2 n_ty values are distinct elements of the row, so their K-th largest
 //     t is <= the row's K-th largest float32 logit (bitwise search over the
 //     order-preserving keys, 32 block counts).
 //  2. One pass over the row's tiles whose largest logit reaches t - 2 eps keeps
-//     every logit >= t - 2 eps (eps as in the general path): the exact top-K are
-//     all among them.
+//     every stored value >= bf16_floor(t - 2 eps) (eps as in the general path),
+//     which includes every logit >= t - 2 eps: the exact top-K are all among them.
 //  3. float64 re-scoring, ranking by (score desc, index asc), first K written.
 // A row this path cannot take (2 n_ty < K, more tile values than TOPS_CAP, more
 // candidates than FAST_CAP) is flagged in rows_todo for the general kernel.
@@ -970,7 +993,7 @@ constexpr int TOPS_CAP = 4096;
 constexpr int FAST_CAP = 1536;
 template <typename T, typename VT>
 __global__ void __launch_bounds__(SEL_THREADS) topk_select_fast_kernel(
-    const float* __restrict__ S, int64_t ld_s, int V, int K, const float2* __restrict__ tops, int64_t ld_tops,
+    const bf16_t* __restrict__ S, int64_t ld_s, int V, int K, const float2* __restrict__ tops, int64_t ld_tops,
     int n_ty, const T* __restrict__ ht, int d, const T* __restrict__ wt, const double* __restrict__ wmax,
     int32_t* __restrict__ idx_out, VT* __restrict__ val_out, int* __restrict__ rows_todo) {
   __shared__ uint32_t keys[TOPS_CAP];
@@ -1008,7 +1031,7 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_fast_kernel(
     __syncthreads();
     if (tot >= K) t = c;
   }
-  const float* s = S + (int64_t)row * ld_s;
+  const bf16_t* s = S + (int64_t)row * ld_s;
   const T* h = ht + (int64_t)row * d;
   double hn = 0.0;
   for (int j = tid; j < d; j += SEL_THREADS) {
@@ -1018,19 +1041,21 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_fast_kernel(
   hn = sqrt(block_sum_256(hn, shd));
   const double eps = 2.0 * (double)d * 0x1p-23 * hn * (*wmax);
   const float thr = __double2float_rd((double)key_float(t) - 2.0 * eps);
+  const float sthr = bf16_floor(thr);
   // 2. candidates.  A vocabulary tile whose largest logit is below the threshold
   // holds none, so only the other tiles are read (one wave per 256-column tile,
-  // 16 bytes per lane; the index test covers the vocabulary tail).
+  // 8 bytes per lane; the index test covers the vocabulary tail).
   const uint32_t thr_key = float_key(thr);
   for (int q = wave; q < n_ty; q += SEL_THREADS / 64) {
     if (keys[2 * q] < thr_key) continue;
     const int v0 = 256 * q + 4 * lane;
     if (v0 >= V) continue;
-    const f32x4 x = *(const f32x4*)(s + v0);
+    const u32x2 x = *(const u32x2*)(s + v0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int v = v0 + e;
-      if (v < V && x[e] >= thr) {
+      const float xe = __uint_as_float(e & 1 ? x[e >> 1] & 0xffff0000u : x[e >> 1] << 16);
+      if (v < V && xe >= sthr) {
         const int pos = atomicAdd(&ncand, 1);
         if (pos < FAST_CAP) cidx[pos] = v;
       }

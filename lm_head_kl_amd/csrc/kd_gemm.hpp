@@ -90,7 +90,7 @@ enum Epi : int {
   EPI_STORE_BF16 = 1,  // P -> bf16 out
   EPI_KL_FWD = 2,      // per-row online (max, sum exp) partials + cached-entry gather
   EPI_KL_DZ = 3,       // dZ = (g/N) exp(z - lse) - (cached-entry weights) -> dZ (and, if given, dZ^T)
-  EPI_TOPK = 4,        // P -> float out, plus the two largest values of each row in the tile
+  EPI_TOPK = 4,        // P -> bf16 out, plus the two largest float32 values of each row in the tile
 };
 
 struct GemmArgs {
@@ -384,7 +384,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_kernel(const GemmArgs a) 
   const int mcol = y0 + wy * WY + (lane >> 4) * 4;
 
   if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_STORE_BF16 || EPI == EPI_TOPK) {
-    typedef typename std::conditional<EPI == EPI_STORE_BF16, bf16_t, float>::type OT;
+    typedef typename std::conditional<EPI == EPI_STORE_BF16 || EPI == EPI_TOPK, bf16_t, float>::type OT;
 #pragma unroll
     for (int i = 0; i < FX; ++i) {
       const int n = nrow0 + i * 16;

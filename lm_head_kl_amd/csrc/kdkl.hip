@@ -116,7 +116,7 @@ kd_status validate(kd_op op, const kd_problem* p, Plan* pl) {
   c = std::min<int64_t>(c, round_up(std::max<int64_t>(pl->N, 1), BX));
   pl->Nc = c;
   pl->V_pad = round_up(pl->V, 64);
-  pl->ld_v = pad_ld(pl->V_pad, op == KD_OP_TOPK_BUILD ? 4 : pl->esz);
+  pl->ld_v = pad_ld(pl->V_pad, op == KD_OP_TOPK_BUILD ? 2 : pl->esz);
   pl->ld_t = pad_ld(pl->Nc, pl->esz);
   pl->n_ty = (int)cdiv(pl->V, BY);
   // 32-bit byte offsets inside one 256-row tile of every GEMM operand
@@ -178,7 +178,7 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     L->ew = take(sizeof(float) * pl.Nc * (pl.K + 1));
     L->flags = take(sizeof(int) * 4);
   } else {
-    L->s = take(sizeof(float) * (size_t)(pl.Nc * pl.ld_v));
+    L->s = take(sizeof(bf16_t) * (size_t)(pl.Nc * pl.ld_v));
     L->bmax = take(sizeof(double) * 1024);
     L->wmax = take(sizeof(double));
     L->overflow = take(sizeof(int) * 4);
@@ -675,7 +675,7 @@ template <typename T, typename VT>
 kd_status topk_impl(const Plan& pl, const Layout& L, const void* ht, const void* wt, int32_t* idx, void* val,
                     char* ws, hipStream_t st) {
   if (pl.N == 0) return KD_OK;
-  float* S = (float*)(ws + L.s);
+  bf16_t* S = (bf16_t*)(ws + L.s);
   double* bmax = (double*)(ws + L.bmax);
   double* wmax = (double*)(ws + L.wmax);
   int* overflow = (int*)(ws + L.overflow);
@@ -702,10 +702,10 @@ kd_status topk_impl(const Plan& pl, const Layout& L, const void* ht, const void*
     g.out_cols = (int)pl.V_pad;
     g.partials = tops;
     g.ld_part = pl.Nc;
-    KD_TRY((run_gemm<T, EPI_TOPK>("gemm_topk", g, 4 * nr * pl.V_pad, st)));
+    KD_TRY((run_gemm<T, EPI_TOPK>("gemm_topk", g, 2 * nr * pl.V_pad, st)));
     // one pass over each row's logits from the tile pairs' bound; rows it cannot take
     // go to the general radix kernel
-    KD_TRY(launch("topk_select", 0.0, 4.0 * nr * pl.V_pad + (double)nr * pl.K * (4 + sizeof(VT)), st, [&] {
+    KD_TRY(launch("topk_select", 0.0, 2.0 * nr * pl.V_pad + (double)nr * pl.K * (4 + sizeof(VT)), st, [&] {
       hipLaunchKernelGGL((topk_select_fast_kernel<T, VT>), dim3(nr), dim3(SEL_THREADS), 0, st, S, pl.ld_v,
                          (int)pl.V, pl.K, (const float2*)tops, pl.Nc, pl.n_ty, hc, (int)pl.d, (const T*)wt, wmax,
                          idx + r0 * pl.K, (VT*)val + r0 * pl.K, todo);

@@ -847,6 +847,18 @@ __device__ __forceinline__ double bf16_logit_lower(float s) {
   return (double)s - (a > 0x1p-133 ? a : 0x1p-133);
 }
 
+// Bound on |float32 MFMA logit - exact logit| for every logit of a row: Higham's
+// summation bound with Cauchy-Schwarz, d 2^-23 ||h|| max_v ||w_v|| (one unit in the
+// last place per operation, any order and rounding direction), doubled to cover a
+// matrix unit that aligns each block of at least three products to the largest
+// exponent and truncates; plus what flushing subnormals can lose: inputs below
+// 2^-126 (at most 2^-126 sqrt(d) (||h|| + max ||w||) over the row) and up to d
+// products and d partial sums (2^-126 each).
+__device__ __forceinline__ double topk_eps(int d, double hn, double wmax) {
+  const double dd = (double)d;
+  return 2.0 * dd * 0x1p-23 * hn * wmax + 0x1p-126 * (sqrt(dd) * (hn + wmax) + 2.0 * dd);
+}
+
 constexpr int SEL_CAP = 6144;    // candidate capacity per row (K <= 4096)
 constexpr int SEL_THREADS = 256;
 
@@ -882,9 +894,8 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, int need, int* 
 //  1. Two 12-bit radix histograms of the order-preserving key locate a
 //     sub-bin [lo, ...) that contains the K-th largest stored value S_K; the K-th
 //     largest float32 logit is >= bf16_logit_lower(lo) =: T.
-//  2. Every logit >= T - 2*eps is a candidate, where eps bounds |fp32 - exact|
-//     for any logit of the row (Higham's summation bound with Cauchy-Schwarz:
-//     eps = 2 d 2^-23 ||h|| max_v ||w_v||); the rounding is monotone, so every
+//  2. Every logit >= T - 2*eps is a candidate, where eps = topk_eps(...) bounds
+//     |fp32 - exact| for any logit of the row; the rounding is monotone, so every
 //     such logit is stored as a value >= bf16_floor(T - 2*eps).  Every exact
 //     top-K member is in the set.
 //  3. Candidates are re-scored in float64 (exact products, a fixed summation order,
@@ -912,7 +923,7 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_kernel(
     hn += x * x;
   }
   hn = sqrt(block_sum_256(hn, shd));
-  const double eps = 2.0 * (double)d * 0x1p-23 * hn * (*wmax);
+  const double eps = topk_eps(d, hn, *wmax);
 
   // pass 1: top 12 bits of the key
   for (int b = tid; b < 4096; b += SEL_THREADS) hist[b] = 0u;
@@ -1039,7 +1050,7 @@ __global__ void __launch_bounds__(SEL_THREADS) topk_select_fast_kernel(
     hn += x * x;
   }
   hn = sqrt(block_sum_256(hn, shd));
-  const double eps = 2.0 * (double)d * 0x1p-23 * hn * (*wmax);
+  const double eps = topk_eps(d, hn, *wmax);
   const float thr = __double2float_rd((double)key_float(t) - 2.0 * eps);
   const float sthr = bf16_floor(thr);
   // 2. candidates.  A vocabulary tile whose largest logit is below the threshold

@@ -121,6 +121,23 @@ def test_topk_rescoring_at_wide_hidden_rows(case):
         np.testing.assert_array_equal(gv.cpu().numpy().view(np.uint32), val.view(np.uint32))
 
 
+def test_topk_subnormal_logits():
+    """Hidden states near 2^-128: nearly all of them, every product and most of the
+    top logits are subnormal.  The cache is still the exact top-K of the float64
+    logits, its values rounded to bf16 subnormals below 2^-126."""
+    n, d, v, k = 64, 64, 3000, 20
+    p = kd_synth.small_problem(n, d, v, seed=23, logit_scale=2.0 ** -128)
+    H = kd_synth.to_float64(p["H"], "bf16")
+    WT = kd_synth.to_float64(p["WT"], "bf16")
+    assert (np.abs(H) < 2.0 ** -126).mean() > 0.99
+    idx, val, sc = oracle.topk_cache(H, WT, k, "bf16")
+    assert (np.abs(sc) < 2.0 ** -126).mean() > 0.9
+    gi, gv = kd.kd_topk_cache_build(to_dev(p["H"], "bf16"), to_dev(p["WT"], "bf16"), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gi.cpu().numpy(), idx)
+    np.testing.assert_array_equal(bf16_bits_of(gv), val)
+
+
 def test_topk_rows_sharing_every_candidate():
     """Half the rows share one hidden state, so every one of them has the same
     candidates and the same near-ties; the other rows interleave with their own."""

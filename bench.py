@@ -411,6 +411,21 @@ def variants(kd, torch, h, wd, idx, val, w, dh_dtype, steps, chunk, ce_weight=0.
     out["student_renorm"] = {"tokens_per_s": n / (rms / 1e3), "ms_per_step": round(rms, 3),
                              "loss": round(r[0].item(), 5)}
     del r
+    # its dominant kernel against HBM bandwidth: the gathered rows (K W rows per token
+    # for the logits and for dH, K H rows per token for dW) are its algorithmic bytes
+    kd.profile_begin()
+    r = rstep()
+    torch.cuda.synchronize()
+    stats = kd.profile_end()
+    del r
+    dom_kind, dom = max(stats.items(), key=lambda kv: kv[1]["total_ms"])
+    avg_s = dom["total_ms"] / dom["launches"] / 1e3
+    achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
+    out["student_renorm"]["roofline"] = {
+        "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": dom_kind, "avg_launch_ms": round(avg_s * 1e3, 4),
+        "bytes_per_launch": dom["bytes"] / dom["launches"]}
+    out["student_renorm"]["kernels_ms_per_step"] = {k2: round(v["total_ms"], 4) for k2, v in stats.items()}
     return out
 
 
@@ -611,9 +626,11 @@ def main() -> int:
     var = None
     if not args.no_variants:
         var = variants(kd, torch, h, wd, idx, val, w, dh_dtype, max(1, min(args.steps, 3)), args.chunk)
+        rr = var["student_renorm"]["roofline"]
         log(f"loss options (mask {100 * var['ignored_frac']:.2f} % of tokens, CE weight {var['ce_weight']}): "
             f"{var['ms_per_step']:.2f} ms/step, {var['tokens_per_s']:.0f} tokens/s; renormalised student: "
-            f"{var['student_renorm']['ms_per_step']:.2f} ms/step, {var['student_renorm']['tokens_per_s']:.0f} tokens/s")
+            f"{var['student_renorm']['ms_per_step']:.2f} ms/step, {var['student_renorm']['tokens_per_s']:.0f} tokens/s, "
+            f"dominant kernel {rr['kernel']} {rr['achieved']:.0f} GB/s of gathered rows ({100 * rr['frac']:.1f} % of HBM)")
 
     cio = None
     if not args.no_cache_io:

@@ -661,113 +661,159 @@ __global__ void __launch_bounds__(256) renorm_dh_kernel(const T* __restrict__ w,
 // dW of the renormalised student, whose dZ is zero off the cached entries:
 //   dW[v] (+)= sum over the chunk's entries with index v of c * H[t]
 // from the chunk's entries bucketed per (256-token, 256-vocabulary) tile in a fixed
-// order, with their gradients c beside them.  One block per vocabulary tile, each wave
-// one vocabulary row at a time: the row's entries are collected in order (token tiles
-// ascending, then the bucket's order) into the wave's LDS list, up to RDW_LIST at a
-// time, and applied in that order to 8 columns per lane; a row with more entries goes
-// through its dW row in pieces (float32 partial sums through memory, the same order).
+// order, with their gradients c beside them.  One block per vocabulary tile.  The
+// tile's entries, in order (token tiles ascending, then each bucket's order), are
+// staged in LDS RDW_PIECE at a time; each wave takes every RDW_WAVES-th vocabulary row
+// of the tile, collects the row's entries of the piece in order into its LDS list (up
+// to RDW_LIST at a time) and applies them in that order to 8 columns per lane, with
+// 16 hidden-row loads in flight.  A row whose entries span several lists or pieces
+// goes through its dW row in float32 partial sums through memory, in the same order.
 // Rows without entries are written as 0, or left as they are when accumulating.
-constexpr int RDW_LIST = 1024;
+constexpr int RDW_WAVES = 8;
+constexpr int RDW_LIST = 512;
+constexpr int RDW_PIECE = 4096;
+constexpr int RDW_SEGS = 256;          // token tiles whose segment offsets are held at a time
 template <typename T>
-__global__ void __launch_bounds__(256) renorm_dw_kernel(const uint32_t* __restrict__ entries,
-                                                        const float* __restrict__ ew, const int* __restrict__ offsets,
-                                                        int n_tx, int n_ty, int kz, const T* __restrict__ h, int d,
-                                                        int vocab, int accumulate, float* __restrict__ dw) {
-  __shared__ int lt[4][RDW_LIST];
-  __shared__ float lc[4][RDW_LIST];
-  const int ty = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ void __launch_bounds__(RDW_WAVES * 64) renorm_dw_kernel(
+    const uint32_t* __restrict__ entries, const float* __restrict__ ew, const int* __restrict__ offsets, int n_tx,
+    int n_ty, int kz, const T* __restrict__ h, int d, int vocab, int accumulate, float* __restrict__ dw) {
+  __shared__ uint32_t pk[RDW_PIECE];   // (token within the chunk) << 8 | vocabulary row within the tile
+  __shared__ float pc[RDW_PIECE];
+  __shared__ int lt[RDW_WAVES][RDW_LIST];
+  __shared__ float lc[RDW_WAVES][RDW_LIST];
+  __shared__ int seg[RDW_SEGS + 1];    // stream position of each held segment's first entry
+  __shared__ int sh[32];
+  const int ty = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int* mt = lt[wave];
   float* mc = lc[wave];
-  for (int vl = wave; vl < 256; vl += 4) {
-    const int v = ty * 256 + vl;
-    if (v >= vocab) break;
+  constexpr int ROWS = 256 / RDW_WAVES;          // vocabulary rows per wave
+  uint64_t touched = 0;                          // bit r: row wave + RDW_WAVES r has been written
+
+  // apply the wave's list (n entries) to dW row v, from 0 or from what the row holds
+  auto apply = [&](int v, int n, bool from_memory) {
     float* out = dw + (int64_t)v * d;
-    int tx = 0;
-    int e = offsets[ty], ee = offsets[ty + 1];
-    bool first = true, done = false;
-    while (!done) {
-      // collect the next RDW_LIST entries of this row, in order
-      int n = 0;
-      while (true) {
-        while (e >= ee && tx + 1 < n_tx) {
-          ++tx;
-          e = offsets[(int64_t)tx * (n_ty + 1) + ty];
-          ee = offsets[(int64_t)tx * (n_ty + 1) + ty + 1];
+    for (int j0 = lane * 8; j0 - lane * 8 < d; j0 += 512) {
+      const bool jin = j0 < d;
+      float acc[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[x] = 0.f;
+      if (jin && from_memory) {
+        const f32x4 a = *(const f32x4*)(out + j0), b = *(const f32x4*)(out + j0 + 4);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          acc[x] = a[x];
+          acc[4 + x] = b[x];
         }
-        if (e >= ee) {
-          done = true;
-          break;
-        }
-        const int q = e + lane;
-        bool m = false;
-        uint32_t u = 0;
-        if (q < ee) {
-          u = entries[(int64_t)tx * BX * kz + q];
-          m = int((u >> 8) & 255u) == vl;
-        }
-        const uint64_t bm = __ballot(m);
-        const int cnt = __builtin_popcountll(bm);
-        if (n + cnt > RDW_LIST) break;     // the list is full: apply it, then resume here
-        if (m) {
-          const int pos = n + lane_rank(bm);
-          mt[pos] = tx * BX + int(u & 255u);
-          mc[pos] = ew[(int64_t)tx * BX * kz + q];
-        }
-        n += cnt;
-        e = min(e + 64, ee);
       }
-      wave_sync_lds();
-      if (n > 0 || (first && !accumulate)) {
-        for (int j0 = lane * 8; j0 - lane * 8 < d; j0 += 512) {
-          const bool jin = j0 < d;
-          float acc[8];
+      for (int q0 = 0; q0 < n; q0 += 16) {
+        const int qn = min(16, n - q0);
+        u32x4 hv[16][sizeof(T) == 2 ? 1 : 2];
 #pragma unroll
-          for (int x = 0; x < 8; ++x) acc[x] = 0.f;
-          if (jin && (!first || accumulate)) {
-            const f32x4 a = *(const f32x4*)(out + j0), b = *(const f32x4*)(out + j0 + 4);
+        for (int q = 0; q < 16; ++q)
+          if (q < qn && jin) {
+            const T* hr = h + (int64_t)mt[q0 + q] * d + j0;
+            hv[q][0] = *(const u32x4*)hr;
+            if constexpr (sizeof(T) == 4) hv[q][sizeof(T) == 2 ? 0 : 1] = *(const u32x4*)(hr + 4);
+          }
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              acc[x] = a[x];
-              acc[4 + x] = b[x];
+        for (int q = 0; q < 16; ++q)
+          if (q < qn && jin) {
+            const float c = mc[q0 + q];
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                acc[2 * x] = fmaf(c, __uint_as_float(hv[q][0][x] << 16), acc[2 * x]);
+                acc[2 * x + 1] = fmaf(c, __uint_as_float(hv[q][0][x] & 0xffff0000u), acc[2 * x + 1]);
+              }
+            } else {
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                acc[x] = fmaf(c, __uint_as_float(hv[q][0][x]), acc[x]);
+                acc[4 + x] = fmaf(c, __uint_as_float(hv[q][sizeof(T) == 2 ? 0 : 1][x]), acc[4 + x]);
+              }
             }
           }
-          for (int q0 = 0; q0 < n; q0 += 16) {
-            const int qn = min(16, n - q0);
-            u32x4 hv[16][sizeof(T) == 2 ? 1 : 2];
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-              if (q < qn && jin) {
-                const T* hr = h + (int64_t)mt[q0 + q] * d + j0;
-                hv[q][0] = *(const u32x4*)hr;
-                if constexpr (sizeof(T) == 4) hv[q][sizeof(T) == 2 ? 0 : 1] = *(const u32x4*)(hr + 4);
-              }
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-              if (q < qn && jin) {
-                const float c = mc[q0 + q];
-                if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                  for (int x = 0; x < 4; ++x) {
-                    acc[2 * x] = fmaf(c, __uint_as_float(hv[q][0][x] << 16), acc[2 * x]);
-                    acc[2 * x + 1] = fmaf(c, __uint_as_float(hv[q][0][x] & 0xffff0000u), acc[2 * x + 1]);
-                  }
-                } else {
-#pragma unroll
-                  for (int x = 0; x < 4; ++x) {
-                    acc[x] = fmaf(c, __uint_as_float(hv[q][0][x]), acc[x]);
-                    acc[4 + x] = fmaf(c, __uint_as_float(hv[q][sizeof(T) == 2 ? 0 : 1][x]), acc[4 + x]);
-                  }
-                }
-              }
+      }
+      if (jin) {
+        *(f32x4*)(out + j0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *(f32x4*)(out + j0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      }
+    }
+  };
+
+  for (int g0 = 0; g0 < n_tx; g0 += RDW_SEGS) {
+    // stream positions of this group's segments (token tiles g0 ..)
+    const int tx = g0 + tid;
+    int len = 0;
+    if (tid < RDW_SEGS && tx < n_tx)
+      len = offsets[(int64_t)tx * (n_ty + 1) + ty + 1] - offsets[(int64_t)tx * (n_ty + 1) + ty];
+    int tot;
+    const int pre = block_excl_scan(tid < RDW_SEGS ? len : 0, sh, tot);
+    if (tid < RDW_SEGS) seg[tid] = pre;
+    if (tid == 0) seg[RDW_SEGS] = tot;
+    __syncthreads();
+    for (int p0 = 0; p0 < tot; p0 += RDW_PIECE) {
+      const int pn = min(RDW_PIECE, tot - p0);
+      // stage the piece: stream position i lies in the last segment starting at or before it
+      for (int i = tid; i < pn; i += RDW_WAVES * 64) {
+        const int sp = p0 + i;
+        int lo = 0, hi = RDW_SEGS;                 // seg[lo] <= sp < seg[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (seg[mid] <= sp) lo = mid;
+          else hi = mid;
+        }
+        const int t = g0 + lo;
+        const int64_t at = (int64_t)t * BX * kz + offsets[(int64_t)t * (n_ty + 1) + ty] + (sp - seg[lo]);
+        const uint32_t u = entries[at];
+        pk[i] = (uint32_t(t * BX + int(u & 255u)) << 8) | ((u >> 8) & 255u);
+        pc[i] = ew[at];
+      }
+      __syncthreads();
+      for (int r = 0; r < ROWS; ++r) {
+        const int vl = wave + RDW_WAVES * r;
+        const int v = ty * 256 + vl;
+        if (v >= vocab) break;
+        int n = 0;
+        for (int i0 = 0; i0 < pn; i0 += 64) {
+          const int q = i0 + lane;
+          uint32_t k = 0;
+          const bool m = q < pn && ((k = pk[q]) & 255u) == (uint32_t)vl;
+          const uint64_t bm = __ballot(m);
+          if (!bm) continue;
+          const int cnt = __builtin_popcountll(bm);
+          if (n + cnt > RDW_LIST) {               // the list is full: apply it and start again
+            wave_sync_lds();
+            apply(v, n, ((touched >> r) & 1) || accumulate);
+            touched |= uint64_t(1) << r;
+            n = 0;
+            wave_sync_lds();                      // the list is read before it is overwritten
           }
-          if (jin) {
-            *(f32x4*)(out + j0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-            *(f32x4*)(out + j0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+          if (m) {
+            const int pos = n + lane_rank(bm);
+            mt[pos] = int(k >> 8);
+            mc[pos] = pc[q];
           }
+          n += cnt;
+        }
+        if (n > 0) {
+          wave_sync_lds();
+          apply(v, n, ((touched >> r) & 1) || accumulate);
+          touched |= uint64_t(1) << r;
+          wave_sync_lds();
         }
       }
-      first = false;
-      wave_sync_lds();   // the list is read before the next piece overwrites it
+      __syncthreads();                            // the piece is read before the next one is staged
+    }
+  }
+  // rows with no entries
+  if (!accumulate) {
+    for (int r = 0; r < ROWS; ++r) {
+      const int v = ty * 256 + wave + RDW_WAVES * r;
+      if (v >= vocab) break;
+      if ((touched >> r) & 1) continue;
+      float* out = dw + (int64_t)v * d;
+      for (int j = lane * 4; j < d; j += 256) *(f32x4*)(out + j) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }

@@ -533,7 +533,7 @@ kd_status bwd_renorm_impl(const Plan& pl, const Layout& L, const void* h, const 
     KD_TRY(run_bucket(pl, idx_c, lab_c, o, 0, nr, pl.K, true, cf, entries, zg, offsets, flags, st));
     KD_TRY(launch("renorm_dw", 2.0 * nr * pl.K * (double)pl.d, (double)nr * pl.K * es * pl.d + 4.0 * pl.V * pl.d, st,
                   [&] {
-      hipLaunchKernelGGL(renorm_dw_kernel<T>, dim3((unsigned)pl.n_ty), dim3(256), 0, st, entries, zg, offsets,
+      hipLaunchKernelGGL(renorm_dw_kernel<T>, dim3((unsigned)pl.n_ty), dim3(RDW_WAVES * 64), 0, st, entries, zg, offsets,
                          (int)cdiv(nr, BX), pl.n_ty, pl.K, hc, (int)pl.d, (int)pl.V, r0 > 0 ? 1 : 0, dw);
     }));
   }

@@ -111,6 +111,29 @@ def test_renorm_whole_vocabulary_equals_the_full_loss():
     assert rel_max_err(to_f64(dw_r), to_f64(dw_f)) <= GRAD_TOL
 
 
+@pytest.mark.parametrize("case", ["one_long_row", "many_token_tiles"])
+def test_renorm_dw_long_rows_and_many_token_tiles(case):
+    """The dW kernel's limits: one vocabulary row holding thousands of a tile's entries
+    (several LDS pieces, each overflowing a wave's row list, so the row's sum goes
+    through partial sums in dW), and a chunk of more than 256 token tiles (the tiles'
+    segment starts held in several groups)."""
+    if case == "one_long_row":
+        n, d, v, k, chunk = 1200, 64, 300, 8, 0
+    else:
+        n, d, v, k, chunk = 66000, 64, 700, 6, 131072
+    H, W, idx, val, dev = _setup(n, d, v, k, "bf16", seed=28, distinct=False)
+    if case == "one_long_row":
+        idx[:, :4] = 5                              # row 5: 4,800 entries, every 4,096-entry piece
+        dev = (dev[0], dev[1], torch.from_numpy(idx).to(device()), dev[3])
+    ref_loss, _, _ = oracle.renorm_forward(H, W, idx, val, 1.0)
+    ref_dH, ref_dW = oracle.renorm_backward(H, W, idx, val, 1.0)
+    loss, lse, rows, dh, dw = _run(dev, 1.0, chunk=chunk)
+    _, _, _, dh2, dw2 = _run(dev, 1.0, chunk=chunk)
+    assert abs(loss.item() - ref_loss) <= LOSS_RTOL * abs(ref_loss)
+    assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL and rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+    assert torch.equal(dh, dh2) and torch.equal(dw, dw2)
+
+
 def test_renorm_single_entry_and_off_set_rows():
     n, d, v = 300, 64, 2000
     H, W, idx, val, dev = _setup(n, d, v, 1, "bf16", seed=26)

@@ -68,8 +68,14 @@ def host_cpu_model() -> str:
 
 class ClockSampler:
     """Samples the GPU's graphics clock (amdsmi, every 25 ms) in a background thread
-    between start() and stop(); stop() returns the mean in MHz, or None when the
-    clock cannot be read (no amdsmi, or not exactly one GPU visible to it)."""
+    between start() and stop(); stop() returns (mean MHz, snapshots), or None when the
+    clock cannot be read (no amdsmi, or not exactly one GPU visible to it) or fewer
+    than two fresh readings came in.  The firmware refreshes its metrics table about
+    once a second, so readings are kept once per table snapshot (its system clock
+    counter), and the snapshot current at start() is left out: it predates the
+    measured work.  A timed region under two seconds therefore reports no clock."""
+
+    MIN_SNAPSHOTS = 2
 
     def __init__(self):
         self.samples = []
@@ -88,17 +94,18 @@ class ClockSampler:
             self.handle = None
 
     def _read(self):
-        # the per-XCD graphics clocks of the GPU metrics table, averaged; else the
-        # clock query's single value
+        # (snapshot id, MHz): the per-XCD graphics clocks of the GPU metrics table,
+        # averaged; else the clock query's single value (no snapshot id)
         try:
             m = self._amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
             xs = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 5000]
+            ts = m.get("system_clock_counter")
             if xs:
-                return sum(xs) / len(xs)
+                return (ts if isinstance(ts, int) else None), sum(xs) / len(xs)
         except Exception:
             pass
         c = self._amdsmi.amdsmi_get_clock_info(self.handle, self._amdsmi.AmdSmiClkType.GFX)
-        return float(c["clk"])
+        return None, float(c["clk"])
 
     def _run(self):
         import time as _t
@@ -113,6 +120,10 @@ class ClockSampler:
         if self.handle is None:
             return
         import threading
+        try:
+            self._stale = self._read()[0]
+        except Exception:
+            self._stale = None
         self.samples = []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
@@ -124,8 +135,16 @@ class ClockSampler:
         self._stop.set()
         self._thread.join()
         self._thread = None
-        s = [x for x in self.samples if x > 0]
-        return (sum(s) / len(s), len(s)) if s else None
+        seen, s = set(), []
+        for ts, mhz in self.samples:
+            if mhz <= 0:
+                continue
+            if ts is not None:
+                if ts == self._stale or ts in seen:
+                    continue
+                seen.add(ts)
+            s.append(mhz)
+        return (sum(s) / len(s), len(s)) if len(s) >= self.MIN_SNAPSHOTS else None
 
 
 def cpu_baseline(workload, n_rows: int, k: int):
@@ -520,7 +539,7 @@ def measure(kd, torch, w, h, wd, idx, val, n, k, steps, warmup, chunk, clock):
     util_clk = None if clk is None else round(mfma_util * 2400.0 / clk[0], 4)
     log(f"{steps} steps: {ms:.2f} ms/step (median {mid:.2f}, min {per_step[0]:.2f}), {n / (ms / 1e3):.0f} tokens/s, "
         f"MFMA {100 * mfma_util:.1f}% of dense peak at 2.4 GHz"
-        + (f", {100 * util_clk:.1f}% at the measured {clock_mhz:.0f} MHz ({clk[1]} samples)" if clk else "")
+        + (f", {100 * util_clk:.1f}% at the measured {clock_mhz:.0f} MHz ({clk[1]} metrics snapshots)" if clk else "")
         + f", peak {peak_gb:.2f} GB, loss={loss_val:.5f}")
     tot = sum(v["total_ms"] for v in stats.values())
     for kind, st in sorted(stats.items(), key=lambda kv: -kv[1]["total_ms"]):

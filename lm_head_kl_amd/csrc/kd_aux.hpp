@@ -448,21 +448,47 @@ __global__ void __launch_bounds__(256) mask_lse_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------------------
 // dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < rows_pad; c < cols.
+// 64 x 64 tiles.  bf16 moves 16 bytes per thread each way (8 columns of a row in,
+// 8 rows of a column out; cols, ld_src and ld_dst are multiples of 8 and rows_pad of
+// 64 where it is used); other types one element per thread.
 template <typename T>
 __global__ void __launch_bounds__(256) transpose_pad_kernel(const T* __restrict__ src, int64_t ld_src, int rows,
                                                             int cols, T* __restrict__ dst, int64_t ld_dst,
                                                             int rows_pad) {
-  __shared__ T tile[64][65];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < rows && c < cols) ? src[(int64_t)r * ld_src + c] : T(0);
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows_pad) dst[(int64_t)c * ld_dst + r] = tile[tx][i];
+  if constexpr (sizeof(T) == 2) {
+    constexpr int P = 72;                          // row pitch: 16-byte aligned rows
+    __shared__ __attribute__((aligned(16))) T tile[64 * P];
+    const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;
+    for (int i = lr; i < 64; i += 32) {
+      const int r = r0 + i, c = c0 + lc;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < rows && c < cols) x = *(const u32x4*)(src + (int64_t)r * ld_src + c);
+      *(u32x4*)(tile + i * P + lc) = x;
+    }
+    __syncthreads();
+    for (int i = lr; i < 64; i += 32) {
+      const int c = c0 + i, r = r0 + lc;
+      if (c < cols && r < rows_pad) {
+        u32x4 y;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          y[q] = uint32_t(tile[(lc + 2 * q) * P + i]) | (uint32_t(tile[(lc + 2 * q + 1) * P + i]) << 16);
+        *(u32x4*)(dst + (int64_t)c * ld_dst + r) = y;
+      }
+    }
+  } else {
+    __shared__ T tile[64][65];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4) {
+      const int r = r0 + i, c = c0 + tx;
+      tile[i][tx] = (r < rows && c < cols) ? src[(int64_t)r * ld_src + c] : T(0);
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+      const int c = c0 + i, r = r0 + tx;
+      if (c < cols && r < rows_pad) dst[(int64_t)c * ld_dst + r] = tile[tx][i];
+    }
   }
 }
 

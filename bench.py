@@ -253,7 +253,37 @@ def sweep(kd, torch, np, kd_synth, steps, warmup):
     for r in rows:
         log(f"| {r['workload']} | {r['n_tokens']:,} | {r['d']:,} | {r['vocab']:,} | {r['k']} | {r['tokens_per_s']:,.0f} | "
             f"{r['ms_per_step']:.2f} | {100 * r['mfma_util']:.1f} % | {r['peak_gb']:.2f} | {r['cache_build_ms']:.1f} |")
+    for fit in peak_memory_fits(np, rows):
+        print(json.dumps(fit), flush=True)
+        log(f"peak memory, {fit['workload']} K={fit['k']}: {fit['intercept_gb']:.3f} GB + {fit['slope_bytes_per_token']:,.0f} "
+            f"B/token (expected {fit['expected_bytes_per_token']:,} = H, bf16 dH, cache, lse), largest residual "
+            f"{100 * fit['max_rel_residual']:.2f} %, over N = {fit['n_tokens']}; an N x V bf16 tensor would add "
+            f"{2 * fit['vocab']:,} B/token")
     return 0
+
+
+def peak_memory_fits(np, rows, chunk=16384):
+    """Least-squares line peak(N) = a + b N per (workload, K) over the sweep points at
+    or above one token chunk (below it the backward's workspace is smaller).  Linear
+    memory means b is the per-token inputs and outputs only: H and dH (2d bytes each in
+    bf16), the cache (4 + 2 bytes per entry) and lse (4 bytes), with no term in V."""
+    out = []
+    groups = {}
+    for r in rows:
+        if r["n_tokens"] >= chunk:
+            groups.setdefault((r["workload"], r["k"]), []).append(r)
+    for (name, k), rs in groups.items():
+        if len(rs) < 3:
+            continue
+        ns = np.array([r["n_tokens"] for r in rs], dtype=np.float64)
+        ps = np.array([r["peak_gb"] * 1e9 for r in rs])
+        b, a = np.polyfit(ns, ps, 1)
+        d = rs[0]["d"]
+        out.append({"peak_memory_fit": True, "workload": name, "k": k, "vocab": rs[0]["vocab"],
+                    "n_tokens": [int(x) for x in ns], "intercept_gb": round(float(a) / 1e9, 4),
+                    "slope_bytes_per_token": round(float(b), 1), "expected_bytes_per_token": 2 * d + 2 * d + 6 * k + 4,
+                    "max_rel_residual": round(float(np.abs(ps - (a + b * ns)).max() / ps.max()), 5)})
+    return out
 
 
 def cache_io(kd, torch, idx, val, vocab, shards=4, batch=16384, prefetch=3, with_paths=None):

@@ -511,11 +511,14 @@ def inputs_and_cache(kd, torch, np, kd_synth, w, n, k, dev, timed=True):
     return h, wd, idx, val, cache
 
 
-def measure(kd, torch, w, h, wd, idx, val, n, k, steps, warmup, chunk, clock):
+def measure(kd, torch, w, h, wd, idx, val, n, k, steps, warmup, chunk, clock, min_seconds=0.0):
     """`warmup` untimed and `steps` timed fwd+bwd steps.  Whole-run wall time gives
     tokens/s; HIP events on the launch stream give each step's time (median, min)
     and, through the library's profiling hooks, each kernel's average launch time
-    (the roofline of the dominant kernel).  The graphics clock is sampled meanwhile."""
+    (the roofline of the dominant kernel).  The graphics clock is sampled meanwhile.
+    With `min_seconds`, more steps are timed if `steps` would take less than that
+    (estimated from the last warmup step), so the clock sampler sees enough of the
+    GPU's metrics snapshots (about one a second)."""
     dev = h.device
     dh_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
@@ -524,10 +527,16 @@ def measure(kd, torch, w, h, wd, idx, val, n, k, steps, warmup, chunk, clock):
         dh, dw = kd.kd_chunked_kl_bwd(h, wd, idx, val, w.tau, lse, None, dh_dtype=dh_dtype, chunk_tokens=chunk)
         return loss, dh, dw
 
-    for i in range(warmup):
+    est = None
+    nwarm = max(warmup, 1 if min_seconds > 0 else 0)
+    for i in range(nwarm):
+        t0 = time.perf_counter()
         wl = step()[0].item()
         torch.cuda.synchronize()
-        log(f"warmup {i + 1}/{warmup} loss={wl:.5f}")
+        est = time.perf_counter() - t0
+        log(f"warmup {i + 1}/{nwarm} loss={wl:.5f}")
+    if min_seconds > 0 and est and steps * est < min_seconds:
+        steps = int(min_seconds / est) + 1
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     base = torch.cuda.memory_allocated(dev)
@@ -591,7 +600,7 @@ def measure(kd, torch, w, h, wd, idx, val, n, k, steps, warmup, chunk, clock):
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom_kind), "kernel": dom_kind,
                 "avg_launch_ms": round(avg_s * 1e3, 4)}
-    return {"workload": w.name, "n_tokens": n, "d": w.d, "vocab": w.vocab, "k": k, "tau": w.tau,
+    return {"workload": w.name, "n_tokens": n, "d": w.d, "vocab": w.vocab, "k": k, "tau": w.tau, "steps": steps,
             "tokens_per_s": round(n / (ms / 1e3), 1), "ms_per_step": round(ms, 3), "ms_median": round(mid, 3),
             "ms_min": round(per_step[0], 3), "mfma_util": round(mfma_util, 4),
             "mfma_util_measured_clock": util_clk, "clock_mhz": clock_mhz, "peak_gb": round(peak_gb, 3),
@@ -707,12 +716,15 @@ def main() -> int:
         torch.cuda.empty_cache()
         wt_ = kd_synth.WORKLOADS["ctx32k_v128k"]
         h, wd, idx, val, tcache = inputs_and_cache(kd, torch, np, kd_synth, wt_, 32768, 100, dev, timed=True)
-        target = measure(kd, torch, wt_, h, wd, idx, val, 32768, 100, args.steps, args.warmup, args.chunk, clock)
+        target = measure(kd, torch, wt_, h, wd, idx, val, 32768, 100, args.steps, args.warmup, args.chunk, clock,
+                         min_seconds=3.0)
         target.pop("_stats")
         target["cache_build"] = tcache
-        log(f"target point ctx32k_v128k: {target['tokens_per_s']:.0f} tokens/s, median {target['ms_median']:.2f} ms, "
-            f"MFMA {100 * target['mfma_util']:.1f}% (at the measured clock {target['mfma_util_measured_clock']}), "
-            f"peak {target['peak_gb']:.2f} GB")
+        uc = target["mfma_util_measured_clock"]
+        log(f"target point ctx32k_v128k ({target['steps']} steps): {target['tokens_per_s']:.0f} tokens/s, "
+            f"median {target['ms_median']:.2f} ms, MFMA {100 * target['mfma_util']:.1f}%"
+            + (f" ({100 * uc:.1f}% at the measured {target['clock_mhz']:.0f} MHz)" if uc is not None else "")
+            + f", peak {target['peak_gb']:.2f} GB")
 
     cpu = None
     if not args.no_cpu_baseline:

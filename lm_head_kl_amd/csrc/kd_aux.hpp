@@ -275,7 +275,8 @@ __device__ __forceinline__ double block_sum_256(double v, double* sh) {
   return sh[0];
 }
 
-// Rows per block and threads per row of the per-row kernels (merge, scatter).
+// Rows per block and threads per row of the per-row kernels (merge, teacher weights,
+// and the renormalised student's merge and coefficients).
 constexpr int RB_ROWS = 16, RB_TPR = 16;
 
 // Combine two (max, sum exp) pairs of one row.

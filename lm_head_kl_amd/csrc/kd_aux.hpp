@@ -845,15 +845,17 @@ __global__ void __launch_bounds__(RDW_WAVES * 64) renorm_dw_kernel(
   }
 }
 
-// out[i] = sum over s of part[s * stride + i], s in order (split-K partial sums).
+// out[i] = sum over s of part[s * stride + i], s in order (split-K partial sums);
+// with `accumulate`, out[i] += that sum (the old value plus the partials' sum).
 template <typename OT>
 __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restrict__ part, int splits,
-                                                           int64_t stride, int64_t n4, OT* __restrict__ out) {
+                                                           int64_t stride, int64_t n4, OT* __restrict__ out,
+                                                           int accumulate) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
     f32x4 a = *(const f32x4*)(part + 4 * i);
     for (int s = 1; s < splits; ++s) a += *(const f32x4*)(part + s * stride + 4 * i);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[4 * i + e] = from_f32<OT>(a[e]);
+    for (int e = 0; e < 4; ++e) out[4 * i + e] = from_f32<OT>(accumulate ? to_f32<OT>(out[4 * i + e]) + a[e] : a[e]);
   }
 }
 

@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <atomic>
 #include <mutex>
+#include <numeric>
 #include <cstring>
 #include <string>
 #include <type_traits>
@@ -137,6 +138,25 @@ int dh_splits(const Plan& pl, int64_t nr) {
   return (int)std::max<int64_t>(1, s);
 }
 
+// dW's output tiles in whole rounds of kMinTiles workgroups, and the rest.  When the
+// tiles past the last whole round would leave most compute units idle for a final
+// round (V = 128,256, d = 4,096: 8,016 tiles, 31 rounds and 80 tiles), those tiles are
+// computed as S split-K partials (at least 8 K stages each) summed afterwards in a
+// fixed order, so the final round takes about 1/S of a tile's time.  Returns S (1: one
+// plain launch) and the X tiles (vocabulary tiles) of the whole rounds.
+int dw_splits(const Plan& pl, int64_t nr64, int64_t* tx_main) {
+  const int64_t n_tx = cdiv(pl.V, BX), n_ty = cdiv(pl.d, BY);
+  const int64_t unit = kMinTiles / std::gcd<int64_t>(kMinTiles, n_ty);   // X tiles per whole rounds
+  const int64_t txm = n_tx / unit * unit;
+  const int64_t rem = (n_tx - txm) * n_ty;
+  *tx_main = txm;
+  if (txm == 0 || rem == 0) return 1;
+  const int64_t stages = cdiv(nr64, MainCfg::KB / pl.esz);
+  int64_t s = std::min<int64_t>(kMaxSplits, kMinTiles / rem);
+  s = std::min<int64_t>(s, stages / 8);
+  return (int)std::max<int64_t>(1, s);
+}
+
 size_t layout(kd_op op, const Plan& pl, Layout* L) {
   size_t cur = 0;
   auto take = [&](size_t bytes) {
@@ -162,12 +182,18 @@ size_t layout(kd_op op, const Plan& pl, Layout* L) {
     // bf16 reads dZ K-major in the dW product; float32 (no transposing LDS read)
     // keeps a transposed copy
     if (pl.xdt == KD_F32) L->dzt = take((size_t)(pl.esz * pl.V_pad * pl.ld_t));
-    // split-K partials of dH: the full chunks and the last, shorter one
+    // split-K partials of dH and of dW's last tiles (one region: each product's partials
+    // are summed before the next product starts), for the full chunks and the last one
     const int64_t last = pl.N % pl.Nc;
     const int64_t full = pl.N >= pl.Nc ? pl.Nc : 0;
     int64_t part = 0;
-    for (int64_t nr : {full, last})
-      if (nr > 0 && dh_splits(pl, nr) > 1) part = std::max<int64_t>(part, dh_splits(pl, nr) * nr * pl.d);
+    for (int64_t nr : {full, last}) {
+      if (nr <= 0) continue;
+      if (dh_splits(pl, nr) > 1) part = std::max<int64_t>(part, dh_splits(pl, nr) * nr * pl.d);
+      int64_t txm = 0;
+      const int sw = dw_splits(pl, round_up(nr, 64), &txm);
+      if (sw > 1) part = std::max<int64_t>(part, sw * (pl.V - txm * BX) * pl.d);
+    }
     if (part) L->dhp = take((size_t)(4 * part));
     L->lse_eff = take(sizeof(float) * (size_t)pl.Nc);
     L->count = take(16);
@@ -645,10 +671,10 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
       KD_TRY(launch("dh_split_sum", 0.0, 4.0 * (S + 1) * nr * pl.d, st, [&] {
         if (pl.dhdt == KD_F32)
           hipLaunchKernelGGL(split_reduce_kernel<float>, dim3(nb), dim3(256), 0, st, part, S, gh.split_stride, n4,
-                             (float*)dh + r0 * pl.d);
+                             (float*)dh + r0 * pl.d, 0);
         else
           hipLaunchKernelGGL(split_reduce_kernel<bf16_t>, dim3(nb), dim3(256), 0, st, part, S, gh.split_stride, n4,
-                             (bf16_t*)dh + r0 * pl.d);
+                             (bf16_t*)dh + r0 * pl.d, 0);
       }));
     } else if (pl.dhdt == KD_F32) {
       gh.out = (float*)dh + r0 * pl.d;
@@ -666,7 +692,39 @@ kd_status bwd_impl(const Plan& pl, const Layout& L, const void* h, const void* w
     gw.out_rows = (int)pl.V;
     gw.out_cols = (int)pl.d;
     gw.accumulate = r0 > 0;
-    KD_TRY((run_gemm<T, EPI_STORE_F32, kKm, 0>("gemm_dw", gw, (r0 > 0 ? 8 : 4) * pl.V * pl.d, st)));
+    int64_t txm = 0;
+    const int SW = dw_splits(pl, nr64, &txm);
+    if (SW > 1) {
+      // the whole rounds of tiles, then the rest as SW partial sums over the chunk's
+      // tokens, added to dW (or stored, for the first chunk) in split order
+      const int64_t vm = txm * BX, vr = pl.V - vm;
+      GemmArgs gm = gw;
+      gm.nx = (int)vm;
+      gm.n_tx = (int)txm;
+      gm.out_rows = (int)vm;
+      KD_TRY((run_gemm<T, EPI_STORE_F32, kKm, 0>("gemm_dw", gm, (r0 > 0 ? 8 : 4) * vm * pl.d, st)));
+      float* part = (float*)(ws + L.dhp);
+      GemmArgs gr = gw;
+      // X rows vm.. : dZ columns (K-major) or dZ^T rows
+      gr.X = (const char*)gw.X + (kKm ? vm * es : vm * gw.ldx * es);
+      gr.nx = (int)vr;
+      gr.n_tx = (int)cdiv(vr, BX);
+      gr.out = part;
+      gr.out_rows = (int)vr;
+      gr.accumulate = 0;
+      gr.splits = SW;
+      gr.split_stride = vr * pl.d;
+      KD_TRY((run_gemm<T, EPI_STORE_F32, kKm, 0>("gemm_dw_tail", gr, 4 * SW * vr * pl.d, st)));
+      const int64_t n4 = vr * pl.d / 4;
+      const unsigned nb = (unsigned)std::min<int64_t>(4096, cdiv(n4, 256));
+      const int acc = r0 > 0;
+      KD_TRY(launch("dw_split_sum", 0.0, 4.0 * (SW + 1 + acc) * vr * pl.d, st, [&] {
+        hipLaunchKernelGGL(split_reduce_kernel<float>, dim3(nb), dim3(256), 0, st, part, SW, gr.split_stride, n4,
+                           dw + vm * pl.d, acc);
+      }));
+    } else {
+      KD_TRY((run_gemm<T, EPI_STORE_F32, kKm, 0>("gemm_dw", gw, (r0 > 0 ? 8 : 4) * pl.V * pl.d, st)));
+    }
   }
   return KD_OK;
 }

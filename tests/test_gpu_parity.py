@@ -198,6 +198,35 @@ def test_split_k_dh(dh_dtype):
     assert torch.equal(dh, dh2)
 
 
+@pytest.mark.parametrize("case", [
+    # N, d, V, chunk, dtype: splits of the tail tiles per chunk
+    (3000, 64, 70000, 2048, "bf16"),    # 274 x 1 tiles: 256 in a whole round, 18 in 4 parts; last chunk unsplit
+    (3000, 200, 70000, 2048, "f32"),    # dZ^T rows (float32): 8 parts, then 3 for the last chunk
+    (2500, 768, 66000, 2048, "bf16"),   # 258 x 3 tiles: 6 past the whole round, in 4 parts
+], ids=lambda c: "x".join(map(str, c)))
+def test_dw_tiles_past_the_last_whole_round(case):
+    """dW's tiles past the last whole round of the compute units are computed as
+    split-K partials and added to dW in a fixed order: vocabularies just past a whole
+    number of rounds, the first chunk storing and the later ones adding, and a last
+    chunk too short to split."""
+    n, d, v, chunk, dtype = case
+    k, tau = 20, 1.3
+    p, H, W, WT, idx, val = _problem(n, d, v, k, dtype, seed=29)
+    ref_dH, ref_dW = oracle.kl_backward(H, W, idx, _val64(val, dtype), tau)
+    h, w = to_dev(p["H"], dtype), to_dev(p["W"], dtype)
+    ti, tv = torch.from_numpy(idx).to(device()), to_dev(val, dtype)
+    _, lse, _ = kd.kd_chunked_kl_fwd(h, w, ti, tv, tau, chunk_tokens=chunk)
+    dh, dw = kd.kd_chunked_kl_bwd(h, w, ti, tv, tau, lse, chunk_tokens=chunk)
+    _, dw2 = kd.kd_chunked_kl_bwd(h, w, ti, tv, tau, lse, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    assert rel_max_err(to_f64(dh), ref_dH) <= GRAD_TOL
+    assert rel_max_err(to_f64(dw), ref_dW) <= GRAD_TOL
+    # the tail rows specifically (vocabulary tiles 256 onwards)
+    tail = slice(256 * 256, v)
+    assert rel_max_err(to_f64(dw)[tail], ref_dW[tail]) <= GRAD_TOL
+    assert torch.equal(dw, dw2)
+
+
 def _tiny_config():
     w = kd_synth.WORKLOADS["tiny_fp32"]
     H = kd_synth.hidden(w, w.tokens[0])

@@ -28,10 +28,18 @@ def _static_inputs(n, d, v, seed):
             torch.from_numpy(labels).to(device()))
 
 
+# (N, d, V, K, chunk): two chunks with ragged tails; and a vocabulary of 274 tiles at
+# d = 64, whose dW runs 256 tiles in one launch and the other 18 as split-K partials
+# with their sum (first chunk; the short last chunk is not split)
+GRAPH_SHAPES = [(1000, 256, 3000, 16, 512), (3000, 64, 70000, 16, 2048)]
+
+
+@pytest.mark.parametrize("shape", GRAPH_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("with_options", [False, True])
-def test_graph_replays_equal_eager(with_options):
-    n, d, v, k, tau, chunk = 1000, 256, 3000, 16, 1.5, 512     # two chunks, ragged tails
-    print(f"[case] graph options={with_options}", flush=True)
+def test_graph_replays_equal_eager(with_options, shape):
+    n, d, v, k, chunk = shape
+    tau = 1.5
+    print(f"[case] graph options={with_options} shape={shape}", flush=True)
     h, w, wt, lab = _static_inputs(n, d, v, seed=51)
     gsc = torch.tensor(0.7, dtype=torch.float32, device=device())
     opt = dict(labels=lab, ignore_index=-100, ce_weight=0.3) if with_options else {}

@@ -227,6 +227,36 @@ def test_dw_tiles_past_the_last_whole_round(case):
     assert torch.equal(dw, dw2)
 
 
+def test_dw_split_launches_where_planned():
+    """The split of dW's last tiles is taken where the planner puts it: at V = 70,000
+    and d = 64 (274 vocabulary tiles, 18 past the whole round) every chunk of 2,048
+    tokens gets a split launch and a sum, the 512-token chunk (8 stages, too short to
+    split) and a vocabulary of whole rounds (V = 65,536) get neither, and FLOP counts
+    add up to the whole product."""
+    k, tau = 8, 1.0
+
+    def kinds(n, d, v, chunk):
+        p = kd_synth.small_problem(n, d, v, seed=31, dtype="bf16")
+        h, w = to_dev(p["H"], "bf16"), to_dev(p["W"], "bf16")
+        idx, val = kd_synth.random_cache(n, v, k, seed=32)
+        ti, tv = torch.from_numpy(idx).to(device()), to_dev(val, "bf16")
+        _, lse, _ = kd.kd_chunked_kl_fwd(h, w, ti, tv, tau, chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        kd.profile_begin()
+        kd.kd_chunked_kl_bwd(h, w, ti, tv, tau, lse, chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        return kd.profile_end()
+
+    st = kinds(4096 + 512, 64, 70000, 2048)           # chunks of 2,048, 2,048 and 512 tokens
+    assert st["gemm_dw"]["launches"] == 3
+    assert st["gemm_dw_tail"]["launches"] == 2 and st["dw_split_sum"]["launches"] == 2
+    # every token's dW product is counted once: 2 V d per token (K rounded up to 64)
+    total = st["gemm_dw"]["flops"] + st["gemm_dw_tail"]["flops"]
+    assert total == 2.0 * 70000 * 64 * (4096 + 512)
+    st = kinds(2048, 64, 65536, 2048)                  # 256 tiles: one whole round
+    assert st["gemm_dw"]["launches"] == 1 and "gemm_dw_tail" not in st
+
+
 def _tiny_config():
     w = kd_synth.WORKLOADS["tiny_fp32"]
     H = kd_synth.hidden(w, w.tokens[0])

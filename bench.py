@@ -70,19 +70,24 @@ def host_cpu_model() -> str:
 
 
 class ClockSampler:
-    """Samples the GPU's graphics clock (amdsmi, every 25 ms) in a background thread
-    between start() and stop(); stop() returns (mean MHz, snapshots), or None when the
-    clock cannot be read (no amdsmi, or not exactly one GPU visible to it) or fewer
-    than two fresh readings came in.  The firmware refreshes its metrics table about
-    once a second, so readings are kept once per table snapshot (its system clock
-    counter), and the snapshot current at start() is left out: it predates the
-    measured work.  A timed region under two seconds therefore reports no clock."""
+    """Samples the GPU's metrics table (amdsmi, every 25 ms) in a background thread
+    between start() and stop(): the graphics clock, the socket power and the
+    firmware's count of time spent at the package power limit (PPT).  stop() returns
+    {"mhz", "snapshots", "power_w", "ppt_frac"}, or None when the clock cannot be read
+    (no amdsmi, or not exactly one GPU visible to it) or fewer than two fresh readings
+    came in; power_w and ppt_frac are None when the table lacks them.  The firmware
+    refreshes the table about once a second, so readings are kept once per table
+    snapshot (its system clock counter), and the snapshot current at start() is left
+    out: it predates the measured work.  ppt_frac is the growth of the PPT residency
+    counter over that of the table's accumulation counter between the first and the
+    last fresh snapshot.  A timed region under two seconds therefore reports nothing."""
 
     MIN_SNAPSHOTS = 2
 
     def __init__(self):
         self.samples = []
         self.handle = None
+        self.power_cap_w = None
         self._stop = None
         self._thread = None
         try:
@@ -93,22 +98,33 @@ class ClockSampler:
                 self.handle = hs[0]
                 self._amdsmi = amdsmi
                 self._read()
+                try:   # reported in microwatts
+                    cap = amdsmi.amdsmi_get_power_cap_info(self.handle).get("power_cap")
+                    self.power_cap_w = round(cap / 1e6, 1) if isinstance(cap, (int, float)) and cap > 0 else None
+                except Exception:
+                    self.power_cap_w = None
         except Exception:
             self.handle = None
 
+    @staticmethod
+    def _num(x):
+        return x if isinstance(x, (int, float)) and not isinstance(x, bool) else None
+
     def _read(self):
-        # (snapshot id, MHz): the per-XCD graphics clocks of the GPU metrics table,
-        # averaged; else the clock query's single value (no snapshot id)
+        # (snapshot id, MHz, W, PPT residency, accumulation counter): the per-XCD
+        # graphics clocks of the GPU metrics table, averaged; else the clock query's
+        # single value (no snapshot id, no power)
         try:
             m = self._amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
             xs = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 5000]
             ts = m.get("system_clock_counter")
             if xs:
-                return (ts if isinstance(ts, int) else None), sum(xs) / len(xs)
+                return ((ts if isinstance(ts, int) else None), sum(xs) / len(xs), self._num(m.get("current_socket_power")),
+                        self._num(m.get("ppt_residency_acc")), self._num(m.get("accumulation_counter")))
         except Exception:
             pass
         c = self._amdsmi.amdsmi_get_clock_info(self.handle, self._amdsmi.AmdSmiClkType.GFX)
-        return None, float(c["clk"])
+        return None, float(c["clk"]), None, None, None
 
     def _run(self):
         import time as _t
@@ -138,16 +154,25 @@ class ClockSampler:
         self._stop.set()
         self._thread.join()
         self._thread = None
-        seen, s = set(), []
-        for ts, mhz in self.samples:
+        seen, kept = set(), []
+        for smp in self.samples:
+            ts, mhz = smp[0], smp[1]
             if mhz <= 0:
                 continue
             if ts is not None:
                 if ts == self._stale or ts in seen:
                     continue
                 seen.add(ts)
-            s.append(mhz)
-        return (sum(s) / len(s), len(s)) if len(s) >= self.MIN_SNAPSHOTS else None
+            kept.append(smp)
+        if len(kept) < self.MIN_SNAPSHOTS:
+            return None
+        watts = [k[2] for k in kept if k[2] is not None and k[2] > 0]
+        ppt = None
+        first, last = kept[0], kept[-1]
+        if None not in (first[3], first[4], last[3], last[4]) and last[4] > first[4]:
+            ppt = max(0.0, min(1.0, (last[3] - first[3]) / (last[4] - first[4])))
+        return {"mhz": sum(k[1] for k in kept) / len(kept), "snapshots": len(kept),
+                "power_w": (sum(watts) / len(watts)) if watts else None, "ppt_frac": ppt}
 
 
 def cpu_baseline(workload, n_rows: int, k: int):
@@ -574,14 +599,20 @@ def measure(kd, torch, w, h, wd, idx, val, n, k, steps, warmup, chunk, clock, mi
     # utilisation against the peak at the clock measured meanwhile (the peak scales with
     # it); a reading that would put the MFMA pipes above their peak is not a clock the
     # kernels ran at (e.g. under a profiler), and is dropped
-    if clk is not None and mfma_util * 2400.0 / clk[0] > 1.0:
-        log(f"clock samples ({clk[0]:.0f} MHz) inconsistent with the measured throughput; not reported")
+    if clk is not None and mfma_util * 2400.0 / clk["mhz"] > 1.0:
+        log(f"clock samples ({clk['mhz']:.0f} MHz) inconsistent with the measured throughput; not reported")
         clk = None
-    clock_mhz = None if clk is None else round(clk[0], 1)
-    util_clk = None if clk is None else round(mfma_util * 2400.0 / clk[0], 4)
+    clock_mhz = None if clk is None else round(clk["mhz"], 1)
+    util_clk = None if clk is None else round(mfma_util * 2400.0 / clk["mhz"], 4)
+    power_w = None if clk is None or clk["power_w"] is None else round(clk["power_w"], 1)
+    ppt = None if clk is None or clk["ppt_frac"] is None else round(clk["ppt_frac"], 4)
     log(f"{steps} steps: {ms:.2f} ms/step (median {mid:.2f}, min {per_step[0]:.2f}), {n / (ms / 1e3):.0f} tokens/s, "
         f"MFMA {100 * mfma_util:.1f}% of dense peak at 2.4 GHz"
-        + (f", {100 * util_clk:.1f}% at the measured {clock_mhz:.0f} MHz ({clk[1]} metrics snapshots)" if clk else "")
+        + (f", {100 * util_clk:.1f}% at the measured {clock_mhz:.0f} MHz ({clk['snapshots']} metrics snapshots)"
+           if clk else "")
+        + (f", {power_w:.0f} W" + (f" of the {clock.power_cap_w:.0f} W cap" if clock.power_cap_w else "")
+           if power_w is not None else "")
+        + (f", at the power limit {100 * ppt:.0f}% of the time" if ppt is not None else "")
         + f", peak {peak_gb:.2f} GB, loss={loss_val:.5f}")
     tot = sum(v["total_ms"] for v in stats.values())
     for kind, st in sorted(stats.items(), key=lambda kv: -kv[1]["total_ms"]):
@@ -606,7 +637,8 @@ def measure(kd, torch, w, h, wd, idx, val, n, k, steps, warmup, chunk, clock, mi
     return {"workload": w.name, "n_tokens": n, "d": w.d, "vocab": w.vocab, "k": k, "tau": w.tau, "steps": steps,
             "tokens_per_s": round(n / (ms / 1e3), 1), "ms_per_step": round(ms, 3), "ms_median": round(mid, 3),
             "ms_min": round(per_step[0], 3), "mfma_util": round(mfma_util, 4),
-            "mfma_util_measured_clock": util_clk, "clock_mhz": clock_mhz, "peak_gb": round(peak_gb, 3),
+            "mfma_util_measured_clock": util_clk, "clock_mhz": clock_mhz, "power_w": power_w,
+            "power_limit_residency": ppt, "peak_gb": round(peak_gb, 3),
             "loss": round(loss_val, 5), "roofline": roof,
             "kernels_ms_per_step": {k2: round(v["total_ms"] / steps, 4) for k2, v in stats.items()},
             "_stats": stats}
@@ -746,6 +778,8 @@ def main() -> int:
         "mfma_util": round(mfma_util, 4), "peak_gb": round(peak_gb, 3),
         "ms_median": main_pt["ms_median"], "ms_min": main_pt["ms_min"],
         "clock_mhz": main_pt["clock_mhz"], "mfma_util_measured_clock": main_pt["mfma_util_measured_clock"],
+        "power_w": main_pt["power_w"], "power_cap_w": clock.power_cap_w,
+        "power_limit_residency": main_pt["power_limit_residency"],
         "roofline": roof, "cpu_baseline": cpu, "target_point": target, "cache_build": cache, "cache_io": cio,
         "loss_options": var,
         "kernels_ms_per_step": {k2: round(s["total_ms"] / args.steps, 4) for k2, s in stats.items()},

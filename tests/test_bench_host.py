@@ -1,7 +1,8 @@
 """Host logic of bench.py that runs without a GPU: the refusal of more than one
 GPU, the least-squares fit of peak memory against N, the clock sampler's
 handling of the GPU metrics table (one reading per snapshot, the snapshot
-current at the start left out), and the traffic table's source-hash guard."""
+current at the start left out, mean power and the share of time at the power
+limit), and the traffic table's source-hash guard."""
 import os
 import subprocess
 import sys
@@ -66,18 +67,26 @@ def _sampler(samples, stale):
 
 def test_clock_sampler_keeps_one_reading_per_snapshot_and_drops_the_stale_one():
     # snapshot 7 was current when the timed region began; 8 and 9 are fresh, each
-    # read several times between refreshes
-    c = _sampler([(7, 2400.0), (7, 2400.0), (8, 1800.0), (8, 1800.0), (9, 1900.0), (9, 1900.0), (9, 1900.0)], 7)
-    mean, n = c.stop()
-    assert n == 2 and abs(mean - 1850.0) < 1e-9
+    # read several times between refreshes: (snapshot, MHz, W, PPT residency, accumulation)
+    c = _sampler([(7, 2400.0, 250, 100, 1000), (7, 2400.0, 250, 100, 1000), (8, 1800.0, 1350, 130, 1040),
+                  (8, 1800.0, 1350, 130, 1040), (9, 1900.0, 1370, 166, 1080), (9, 1900.0, 1370, 166, 1080),
+                  (9, 1900.0, 1370, 166, 1080)], 7)
+    r = c.stop()
+    assert r["snapshots"] == 2 and abs(r["mhz"] - 1850.0) < 1e-9
+    assert abs(r["power_w"] - 1360.0) < 1e-9
+    # PPT residency grew by 36 of the accumulation counter's 40 between the fresh snapshots
+    assert abs(r["ppt_frac"] - 0.9) < 1e-12
 
 
 def test_clock_sampler_reports_nothing_from_fewer_than_two_snapshots():
-    assert _sampler([(7, 2400.0), (8, 1800.0), (8, 1800.0)], 7).stop() is None
+    assert _sampler([(7, 2400.0, 250, 1, 1), (8, 1800.0, 1300, 2, 2), (8, 1800.0, 1300, 2, 2)], 7).stop() is None
     assert _sampler([], 7).stop() is None
-    # readings without a snapshot id (the clock query) each count; non-positive ones never
-    mean, n = _sampler([(None, 1700.0), (None, 0.0), (None, 1900.0)], None).stop()
-    assert n == 2 and abs(mean - 1800.0) < 1e-9
+    # readings without a snapshot id (the clock query) each count; non-positive ones
+    # never; without power fields the power and residency are None
+    r = _sampler([(None, 1700.0, None, None, None), (None, 0.0, None, None, None),
+                  (None, 1900.0, None, None, None)], None).stop()
+    assert r["snapshots"] == 2 and abs(r["mhz"] - 1800.0) < 1e-9
+    assert r["power_w"] is None and r["ppt_frac"] is None
 
 
 def test_traffic_table_is_ignored_once_the_kernel_sources_change(monkeypatch):
